@@ -1,0 +1,193 @@
+/*
+ * libmoe355 -- FP8 block-scale Mixture-of-Experts layer for MI355X (gfx950).
+ *
+ * The operations follow "Accelerate DeepSeek-R1 Inference: Integrate AITER
+ * into SGLang" (rocm.blogs.amd.com): section "Complete MoE Implementation"
+ * (Top-K routing, MoE Sorting, Blockscale FP8 MoE Computation) and section
+ * "General Linear Layer" (FP8 block-scale GEMM).  FP8 is OCP E4M3
+ * (e4m3fn: bias 7, no infinities, largest finite 448).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer argument is a caller-owned DEVICE pointer unless noted.
+ *    The library never allocates device memory and keeps no state between
+ *    calls; workspace is passed in by the caller, sized by the *_sizes /
+ *    *_workspace queries (which are host-only and touch no GPU).
+ *  - Every compute call is asynchronous and ordered on `stream`
+ *    (0 = the default stream).  No call synchronises the host.
+ *  - bf16 tensors are passed as their uint16_t bit patterns, e4m3 tensors as
+ *    uint8_t codes.  Scales are fp32 dequantisation multipliers:
+ *    value = decode(code) * scale.
+ *  - Strides (ld_*, sstride_*) are in elements.
+ *  - Return value: MOE355_OK (0) or a negative status (below).  When an
+ *    argument check fails nothing is launched and no memory is touched.
+ *    A launch failure reported by the runtime returns MOE355_ELAUNCH.
+ *  - A call with zero tokens / rows is a successful no-op.
+ */
+#ifndef MOE355_H
+#define MOE355_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE355_OK 0
+#define MOE355_EINVAL (-1)       /* null pointer, negative size, ld < width, workspace too small */
+#define MOE355_EUNSUPPORTED (-2) /* shape or option outside what the kernels implement */
+#define MOE355_EMISALIGNED (-3)  /* a base pointer or row stride breaks the 16-byte alignment rule */
+#define MOE355_ELAUNCH (-4)      /* the HIP runtime reported an error at launch */
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* moe355_strerror(int status);
+
+/*
+ * Biased grouped top-k routing ("Complete MoE Implementation" / "Top-K
+ * routing": tokens choose a fixed number of expert groups, then their top-k
+ * experts inside those groups; a correction bias steers the choice; optional
+ * renormalisation; the routed scaling factor multiplies the weights).
+ *
+ * Per token t (fl32 = round to fp32, nearest-even):
+ *   s_e  = fl32(1/(1+exp(-logits[t,e])))  (evaluated in binary64)
+ *   b_e  = fl32(s_e + bias[e])
+ *   group g = experts [g*E/n_group, (g+1)*E/n_group); score = fl32(top1 + top2 of b)
+ *   keep the topk_group best groups (score desc, group index asc)
+ *   topk_ids[t, 0..topk)  = best experts of the kept groups by (b desc, id asc), in that order
+ *   topk_weights[t, j]    = s of that expert; if renorm: divided by the fp32
+ *                           left-to-right sum of the row; then * routed_scaling_factor.
+ *
+ * logits        fp32 [T, E], row stride ld_logits >= E.
+ * bias          fp32 [E] (the correction bias).
+ * topk_weights  fp32 [T, topk] out, row stride ld_topk >= topk.
+ * topk_ids      int32 [T, topk] out, same row stride ld_topk.
+ * Supported: 1 <= E <= 1024, E % n_group == 0, E/n_group >= 2, n_group <= 64,
+ *            1 <= topk_group <= n_group, 1 <= topk <= min(32, topk_group*E/n_group).
+ */
+int grouped_topk(const float* logits, int64_t ld_logits, const float* bias,
+                 int T, int E, int n_group, int topk_group, int topk,
+                 int renorm, float routed_scaling_factor,
+                 float* topk_weights, int32_t* topk_ids, int64_t ld_topk,
+                 hipStream_t stream);
+
+/*
+ * Host-only size query for moe_sort (no GPU access).
+ *   max_sorted      = capacity of sorted_ids / sorted_weights: T*topk + E*(block_m-1),
+ *                     rounded up to block_m;
+ *   max_blocks      = max_sorted / block_m = capacity of sorted_expert_ids;
+ *   workspace_bytes = device scratch moe_sort needs.
+ * Any output pointer may be NULL.  block_m must be 16, 32, 64 or 128.
+ */
+int moe_sort_sizes(int T, int topk, int E, int block_m,
+                   int64_t* max_sorted, int64_t* max_blocks, size_t* workspace_bytes);
+
+/*
+ * MoE align/sort ("Complete MoE Implementation" / "MoE Sorting": token-expert
+ * pairs bucketed per expert for the grouped GEMM).  Pairs are flattened as
+ * p = t*topk + j.  For experts in ascending order, expert e's pairs occupy a
+ * segment of sorted_ids in ascending p, padded with the sentinel T*topk (weight
+ * 0.0f) up to a multiple of block_m; experts without pairs get no segment.
+ *   sorted_ids        int32 [max_sorted] out: flat pair index or sentinel
+ *   sorted_weights    fp32  [max_sorted] out: topk_weights of the pair, 0 for padding
+ *   sorted_expert_ids int32 [max_blocks] out: expert of each block_m-row block
+ *   num_valid         int32 [1] out: padded total P (entries at or beyond P are
+ *                     left untouched); -1 if an id lies outside [0, E)
+ * topk_ids / topk_weights: [T, topk] with row stride ld_topk.
+ * workspace: device memory of at least workspace_bytes (moe_sort_sizes); its
+ * contents need no initialisation and are scratch after the call.
+ * block_m must equal the block_m later passed to the grouped GEMMs.
+ */
+int moe_sort(const int32_t* topk_ids, const float* topk_weights, int64_t ld_topk,
+             int T, int topk, int E, int block_m,
+             int32_t* sorted_ids, float* sorted_weights, int32_t* sorted_expert_ids,
+             int32_t* num_valid, void* workspace, size_t workspace_bytes,
+             hipStream_t stream);
+
+/*
+ * Dynamic 1x128 FP8 quantisation ("General Linear Layer": one scale per 1x128
+ * of an activation row; "Blockscale FP8 MoE Computation": the bf16 hidden
+ * states are quantised per 128 before the grouped GEMM).  Per row m and
+ * group kb (columns [128*kb, 128*kb+128)):
+ *   amax  = max |x|;  scale = (amax == 0) ? 1 : fl32(amax / 448)
+ *   q     = e4m3(fl32(x / scale))  nearest-even, saturating at +-448, sign kept
+ * x      bf16 bits [M, K], row stride ld_x >= K.
+ * q      e4m3 [M, K] out, row stride ld_q >= K.
+ * scale  fp32 out, element (m, kb) at scale[m*sstride_m + kb*sstride_kb]:
+ *        row-major [M, K/128] is (K/128, 1); K-block-major [K/128, M] is (1, M).
+ * K % 128 == 0.  x, q and their row strides (in bytes) must be 16-byte aligned.
+ */
+int fp8_quant_1x128(const uint16_t* x, int64_t ld_x, int M, int K,
+                    uint8_t* q, int64_t ld_q,
+                    float* scale, int64_t sstride_m, int64_t sstride_kb,
+                    hipStream_t stream);
+
+/*
+ * Gate/up grouped GEMM with SiLU(gate)*up ("Blockscale FP8 MoE Computation":
+ * grouped GEMM over the sorted pairs with fused gate/up weights, g1u1).
+ * For every valid row r of the sorted buffer (r < num_valid, sorted_ids[r] < T*topk),
+ * token t = sorted_ids[r] / topk, expert e = sorted_expert_ids[r / block_m]:
+ *   acc[n] = sum_kb a_scale(t,kb) * w1_scale[e, n/128, kb] * sum_{k in kb} a8[t,k] * w1[e,n,k]
+ *   h[i]   = SiLU(acc[i]) * acc[I+i],  i < I            (fp32)
+ *   h8[r, :], h_scale[r, :] = 1x128 quantisation of h (same rule as fp8_quant_1x128)
+ * a8        e4m3 [T, H] (row stride H); a_scale(t,kb) = a_scale[t*sstride_m + kb*sstride_kb].
+ * w1        e4m3 [E, 2I, H]: rows [0, I) gate, [I, 2I) up;  w1_scale fp32 [E, 2I/128, H/128].
+ * sorted_*  / num_valid as written by moe_sort with the same block_m; max_sorted
+ *           is the capacity returned by moe_sort_sizes.
+ * h8        e4m3 [max_sorted, I] out; h_scale fp32 [max_sorted, I/128] out.
+ *           Padding rows and rows at or beyond num_valid are not written.
+ * H % 128 == 0, I % 128 == 0, block_m in {16, 32, 64, 128}; a8, w1, h8 16-byte aligned.
+ */
+int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale,
+                            int64_t sstride_m, int64_t sstride_kb,
+                            const uint8_t* w1, const float* w1_scale,
+                            const int32_t* sorted_ids, const int32_t* sorted_expert_ids,
+                            const int32_t* num_valid,
+                            int T, int H, int I, int E, int topk, int block_m, int64_t max_sorted,
+                            uint8_t* h8, float* h_scale, hipStream_t stream);
+
+/* Host-only workspace query for moe_down_combine (no GPU access). */
+int moe_down_combine_workspace(int T, int H, int topk, size_t* bytes);
+
+/*
+ * Down-projection grouped GEMM and top-k-weighted combine ("Blockscale FP8
+ * MoE Computation": the second expert GEMM and the weighted sum of each
+ * token's expert outputs into the [tokens, model_dim] output).
+ *   y[r, n]  = sum_kb h_scale[r,kb] * w2_scale[e, n/128, kb] * sum_{k in kb} h8[r,k] * w2[e,n,k]
+ *   out[t,n] = bf16(sum over j ascending of sorted_weights[r(t,j)] * y[r(t,j), n])
+ * where r(t,j) is the sorted row holding pair t*topk+j (fp32 sums, bf16 nearest-even).
+ * h8 / h_scale  as written by moe_fp8_blockscale_g1u1 ([max_sorted, I], [max_sorted, I/128]).
+ * w2        e4m3 [E, H, I]; w2_scale fp32 [E, H/128, I/128].
+ * out       bf16 bits [T, H] out, row stride ld_out >= H (16-byte aligned rows).
+ * workspace device memory of at least moe_down_combine_workspace() bytes.
+ * Every pair of the T*topk must appear in the sorted buffer (moe_sort guarantees it).
+ */
+int moe_down_combine(const uint8_t* h8, const float* h_scale,
+                     const uint8_t* w2, const float* w2_scale,
+                     const int32_t* sorted_ids, const float* sorted_weights,
+                     const int32_t* sorted_expert_ids, const int32_t* num_valid,
+                     int T, int H, int I, int E, int topk, int block_m, int64_t max_sorted,
+                     uint16_t* out, int64_t ld_out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * Dense FP8 block-scale GEMM ("General Linear Layer": Y = (XQ, 1x128 scales)
+ * times (WQ, 128x128 scales)^T with WQ stored [N, K]):
+ *   c[m,n] = bf16( sum_kb a_scale(m,kb) * b_scale[n/128, kb] * sum_{k in kb} a8[m,k] * b8[n,k] )
+ * a8       e4m3 [M, K] (row stride K); a_scale(m,kb) = a_scale[m*sstride_m + kb*sstride_kb].
+ * b8       e4m3 [N, K] (row stride K); b_scale fp32 [N/128, K/128].
+ * c        bf16 bits [M, N] out, row stride ldc >= N.
+ * K % 128 == 0, N % 128 == 0; a8, b8 16-byte aligned.
+ */
+int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale,
+                        int64_t sstride_m, int64_t sstride_kb,
+                        const uint8_t* b8, const float* b_scale,
+                        int M, int N, int K, uint16_t* c, int64_t ldc,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE355_H */

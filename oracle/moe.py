@@ -1,0 +1,111 @@
+"""FP8 block-scale MoE expert computation (CPU oracle; test infrastructure only).
+
+"Accelerate DeepSeek-R1 Inference: Integrate AITER into SGLang", section
+"Complete MoE Implementation" / "Blockscale FP8 MoE Computation": a grouped
+GEMM over the sorted token-expert pairs with fused gate/up weights (g1u1:
+w1 has twice the rows of w2's inner dimension), SiLU(gate) * up, a down
+projection, and the combine of each token's top-k expert outputs weighted
+by sorted_weight_buf into the [tokens, model_dim] output.
+
+Layouts: w1 [E, 2I, H] (rows [0, I) gate, [I, 2I) up), w1_scale
+[E, 2I/128, H/128]; w2 [E, H, I], w2_scale [E, H/128, I/128]; a8 [T, H] with
+a_scale [T, H/128].
+
+Readings taken where the page hides the step inside its fused kernel:
+  * the intermediate h = fl32(SiLU(g) * u), SiLU(g) = g / (1 + exp(-g)) in
+    binary64, is requantised with the same dynamic 1x128 rule as the
+    activations before the down projection (both products on FP8);
+  * the routing weight multiplies each pair's down-projection output, and a
+    token's k weighted outputs are summed in ascending j, in binary64.
+"""
+import numpy as np
+
+from . import gemm, quant
+
+
+def silu_mul_f32(g, u):
+    """fl32(SiLU(g) * u) with the products in binary64."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+
+
+def expert_ffn_h(a8_rows, a_scale_rows, w1_e, w1_scale_e):
+    """Gate/up GEMM for rows of one expert -> (h float32 [R, I], acc float64 [R, 2I])."""
+    acc = gemm.gemm_blockscale(a8_rows, a_scale_rows, w1_e, w1_scale_e)
+    I = acc.shape[1] // 2
+    return silu_mul_f32(acc[:, :I], acc[:, I:]), acc
+
+
+def g1u1(a8, a_scale, w1, w1_scale, sorted_ids, sorted_expert_ids, num_valid, topk, block_m):
+    """Gate/up stage over the sorted buffer.
+
+    Returns (h8 uint8 [P, I], h_scale float32 [P, I/128], h float32 [P, I], valid bool [P]);
+    rows holding the sentinel are left zero and marked invalid.
+    """
+    T = a8.shape[0]
+    E, twoI, H = w1.shape
+    I = twoI // 2
+    P = int(num_valid)
+    h = np.zeros((P, I), dtype=np.float32)
+    valid = np.asarray(sorted_ids[:P]) < T * topk
+    for blk in range(P // block_m):
+        rows = np.arange(blk * block_m, (blk + 1) * block_m)
+        rows = rows[valid[rows]]
+        if len(rows) == 0:
+            continue
+        e = int(sorted_expert_ids[blk])
+        tok = np.asarray(sorted_ids)[rows] // topk
+        h[rows], _ = expert_ffn_h(a8[tok], a_scale[tok], w1[e], w1_scale[e])
+    h8, hs = quant.quant_1x128(h)
+    h8[~valid] = 0
+    hs[~valid] = 0
+    return h8, hs, h, valid
+
+
+def down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sorted_expert_ids,
+                 num_valid, T, topk, block_m):
+    """Down projection + weighted combine -> ref float64 [T, H] (before the bf16 store)."""
+    E, H, I = w2.shape
+    P = int(num_valid)
+    sid = np.asarray(sorted_ids)
+    y = np.zeros((T * topk, H), dtype=np.float64)       # per pair, weight applied
+    for blk in range(P // block_m):
+        rows = np.arange(blk * block_m, (blk + 1) * block_m)
+        rows = rows[sid[rows] < T * topk]
+        if len(rows) == 0:
+            continue
+        e = int(sorted_expert_ids[blk])
+        yy = gemm.gemm_blockscale(h8[rows], h_scale[rows], w2[e], w2_scale[e])
+        y[sid[rows]] = np.asarray(sorted_weights, dtype=np.float64)[rows, None] * yy
+    out = np.zeros((T, H), dtype=np.float64)
+    y = y.reshape(T, topk, H)
+    for j in range(topk):
+        out += y[:, j, :]
+    return out
+
+
+def layer_tokens(tokens, a8, a_scale, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights):
+    """Token-major evaluation of the expert part of the layer for selected tokens.
+
+    Uses no sort buffer: for each token t and slot j, expert ids[t, j] is
+    applied to row t directly.  Returns (ref float64 [len(tokens), H],
+    h8 uint8 [len, k, I], h_scale float32 [len, k, I/128]).
+    """
+    tokens = np.asarray(tokens, dtype=np.int64)
+    E, H, I = w2.shape
+    k = topk_ids.shape[1]
+    ref = np.zeros((len(tokens), H), dtype=np.float64)
+    h8s = np.zeros((len(tokens), k, I), dtype=np.uint8)
+    hss = np.zeros((len(tokens), k, I // 128), dtype=np.float32)
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            e = int(topk_ids[t, j])
+            h, _ = expert_ffn_h(a8[t:t + 1], a_scale[t:t + 1], w1[e], w1_scale[e])
+            h8, hs = quant.quant_1x128(h)
+            y = gemm.gemm_blockscale(h8, hs, w2[e], w2_scale[e])[0]
+            ref[i] += np.float64(topk_weights[t, j]) * y
+            h8s[i, j] = h8[0]
+            hss[i, j] = hs[0]
+    return ref, h8s, hss

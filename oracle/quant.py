@@ -1,0 +1,41 @@
+"""Dynamic 1x128 FP8 quantisation (CPU oracle; test infrastructure only).
+
+"Accelerate DeepSeek-R1 Inference: Integrate AITER into SGLang", section
+"General Linear Layer": every 1x128 run of an activation row carries one
+scale; section "Blockscale FP8 MoE Computation" (asm_moe) quantises the
+bf16 hidden states viewed as rows of 128 with one scale per row.
+
+Reading taken for the steps the page leaves open, per group x[0..127]:
+  amax  = max |x_i|                           (exact)
+  scale = 1.0 if amax == 0 else fl32(amax / 448)   (IEEE fp32 division)
+  q_i   = encode(fl32(x_i / scale))           (IEEE fp32 division, RNE,
+                                               saturating, sign kept)
+The scale is a dequantisation multiplier: value = decode(q) * scale.
+"""
+import numpy as np
+
+from . import fp8
+
+GROUP = 128
+
+
+def quant_1x128(x):
+    """x: float32 [M, K], K % 128 == 0 -> (q uint8 [M, K], scale float32 [M, K/128])."""
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    assert K % GROUP == 0
+    g = x.reshape(M, K // GROUP, GROUP)
+    amax = np.max(np.abs(g), axis=2)                                     # float32, exact
+    scale = np.divide(amax, np.float32(fp8.E4M3_MAX), dtype=np.float32)  # fl32(amax/448)
+    scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
+    y = np.divide(g, scale[:, :, None], dtype=np.float32)               # fl32(x/scale)
+    q = fp8.encode(y).reshape(M, K)
+    return q, scale
+
+
+def dequant_1x128(q, scale):
+    """decode(q) * scale per 1x128 group, binary64."""
+    q = np.asarray(q, dtype=np.uint8)
+    M, K = q.shape
+    v = fp8.decode(q).reshape(M, K // GROUP, GROUP)
+    return (v * np.asarray(scale, dtype=np.float64)[:, :, None]).reshape(M, K)

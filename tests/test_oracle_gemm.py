@@ -1,0 +1,43 @@
+"""Pins of the oracle's block-scaled FP8 GEMM."""
+import numpy as np
+import torch
+
+from oracle import fp8, gemm
+
+
+def _codes(rng, shape):
+    c = rng.integers(0, 0x7F, size=shape).astype(np.uint8)       # finite magnitudes
+    return c | (rng.integers(0, 2, size=shape).astype(np.uint8) << 7)
+
+
+def test_block_sums_exact_against_integers(rng):
+    a = _codes(rng, (9, 384))
+    b = _codes(rng, (128, 384))
+    bs = gemm.block_sums(a, b)
+    ai = np.rint(fp8.decode(a) * 512).astype(np.int64)               # e4m3 * 2^9 is an integer
+    bi = np.rint(fp8.decode(b) * 512).astype(np.int64)
+    for kb in range(3):
+        exact = ai[:, kb * 128:(kb + 1) * 128] @ bi[:, kb * 128:(kb + 1) * 128].T
+        assert np.array_equal(bs[kb], exact.astype(np.float64) / 2.0 ** 18)
+
+
+def test_identity_weight_reproduces_input(rng):
+    K = 256
+    a = _codes(rng, (5, K))
+    b = np.zeros((K, K), np.uint8)
+    b[np.arange(K), np.arange(K)] = 0x38                             # 1.0 on the diagonal
+    out = gemm.gemm_blockscale(a, np.ones((5, 2), np.float32), b, np.ones((2, 2), np.float32))
+    assert np.array_equal(out, fp8.decode(a))
+
+
+def test_against_dequantised_torch_matmul(rng):
+    M, N, K = 7, 256, 512
+    a = _codes(rng, (M, K)) & 0xF7
+    b = _codes(rng, (N, K)) & 0xF7
+    sa = rng.random((M, K // 128)).astype(np.float32) + 0.1
+    sb = rng.random((N // 128, K // 128)).astype(np.float32) + 0.1
+    out = gemm.gemm_blockscale(a, sa, b, sb)
+    A = torch.from_numpy(fp8.decode(a) * np.repeat(sa.astype(np.float64), 128, axis=1))
+    B = torch.from_numpy(fp8.decode(b) * np.repeat(np.repeat(sb.astype(np.float64), 128, 0), 128, 1))
+    ref = (A @ B.T).numpy()
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())

@@ -1,0 +1,79 @@
+"""Pins of the oracle's expert stages and their composition."""
+import math
+
+import numpy as np
+import torch
+
+from oracle import fp8, moe, quant, routing, sort
+
+
+def test_silu_mul_closed_forms():
+    g = np.array([0.0, math.log(3.0), -math.log(3.0), 50.0, -800.0], np.float64)
+    u = np.array([5.0, 2.0, 2.0, 1.0, 1.0])
+    h = moe.silu_mul_f32(g, u)
+    # SiLU(0)=0; sigmoid(ln 3) = 3/4; sigmoid(-ln 3) = 1/4; SiLU(50) ~ 50; SiLU(-800) -> -0
+    exp = np.float32([0.0, 0.75 * math.log(3.0) * 2, -0.25 * math.log(3.0) * 2, 50.0, 0.0])
+    assert np.allclose(h, exp, rtol=1e-6, atol=0)
+    t = torch.nn.functional.silu(torch.tensor(g)) * torch.tensor(u)
+    assert np.array_equal(h, t.numpy().astype(np.float32))
+
+
+def _small_layer(rng, T=6, H=256, I=128, E=4, k=2):
+    x = (rng.standard_normal((T, H))).astype(np.float32)
+    a8, sa = quant.quant_1x128(x)
+    w1 = rng.integers(0, 0x7F, (E, 2 * I, H)).astype(np.uint8) & 0x3F | (rng.integers(0, 2, (E, 2 * I, H)).astype(np.uint8) << 7)
+    w2 = rng.integers(0, 0x7F, (E, H, I)).astype(np.uint8) & 0x3F | (rng.integers(0, 2, (E, H, I)).astype(np.uint8) << 7)
+    s1 = (rng.random((E, 2 * I // 128, H // 128)) * 0.01).astype(np.float32)
+    s2 = (rng.random((E, H // 128, I // 128)) * 0.01).astype(np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    G = 2 if E >= 4 else 1
+    w, ids = routing.grouped_topk(logits, np.zeros(E, np.float32), G, G, k, True, 2.5)
+    return a8, sa, w1, s1, w2, s2, w, ids
+
+
+def test_sorted_path_equals_token_major(rng):
+    a8, sa, w1, s1, w2, s2, w, ids = _small_layer(rng)
+    T, k = ids.shape
+    for BM in (16, 64):
+        sid, sw, seid, P = sort.moe_sort(ids, w, w1.shape[0], BM)
+        h8, hs, h, valid = moe.g1u1(a8, sa, w1, s1, sid, seid, P, k, BM)
+        out = moe.down_combine(h8, hs, w2, s2, sid, sw, seid, P, T, k, BM)
+        ref, h8t, hst = moe.layer_tokens(np.arange(T), a8, sa, w1, s1, w2, s2, ids, w)
+        assert np.array_equal(out, ref)
+        for r in np.nonzero(valid)[0]:
+            t, j = divmod(int(sid[r]), k)
+            assert np.array_equal(h8[r], h8t[t, j]) and np.array_equal(hs[r], hst[t, j])
+
+
+def test_gate_up_selection_gives_silu_times_value(rng):
+    # gate row i and up row i both pick input column i: h_i = SiLU(a_i) * a_i
+    T, H, I, E = 3, 256, 128, 1
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    a8, sa = quant.quant_1x128(x)
+    w1 = np.zeros((E, 2 * I, H), np.uint8)
+    w1[0, np.arange(I), np.arange(I)] = 0x38
+    w1[0, I + np.arange(I), np.arange(I)] = 0x38
+    s1 = np.ones((E, 2, 2), np.float32)
+    ids = np.zeros((T, 1), np.int32)
+    sid, sw, seid, P = sort.moe_sort(ids, np.ones((T, 1), np.float32), E, 16)
+    h8, hs, h, valid = moe.g1u1(a8, sa, w1, s1, sid, seid, P, 1, 16)
+    a = torch.tensor(fp8.decode(a8[:, :I]) * sa[:, :1].astype(np.float64))
+    expect = (torch.nn.functional.silu(a) * a).numpy().astype(np.float32)
+    assert np.array_equal(h[:T], expect)
+
+
+def test_topk1_identity_down_returns_dequantised_h(rng):
+    # topk=1 with renorm and factor 1 gives weight exactly 1; w2 = identity (H = I), unit scales
+    T, H, I, E = 4, 128, 128, 2
+    a8, sa, w1, s1, _, _, _, _ = _small_layer(rng, T=T, H=H, I=I, E=E, k=1)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    w, ids = routing.grouped_topk(logits, np.zeros(E, np.float32), 1, 1, 1, True, 1.0)
+    assert np.all(w == 1.0)
+    w2 = np.zeros((E, H, I), np.uint8)
+    w2[:, np.arange(H), np.arange(I)] = 0x38
+    s2 = np.ones((E, 1, 1), np.float32)
+    sid, sw, seid, P = sort.moe_sort(ids, w, E, 16)
+    h8, hs, h, valid = moe.g1u1(a8, sa, w1, s1, sid, seid, P, 1, 16)
+    out = moe.down_combine(h8, hs, w2, s2, sid, sw, seid, P, T, 1, 16)
+    for r in np.nonzero(valid)[0]:
+        assert np.array_equal(out[sid[r]], quant.dequant_1x128(h8[r:r + 1], hs[r:r + 1])[0])
