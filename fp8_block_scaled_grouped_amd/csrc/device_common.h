@@ -1,0 +1,55 @@
+// Device helpers shared by the libmoe355 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe355 {
+
+constexpr int kWave = 64;
+constexpr float kE4M3Max = 448.0f;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> OCP e4m3fn code: nearest, ties to even mantissa, saturating at
+// +-448, sign kept (so -0 and negative underflow give 0x80).  Integer ops
+// only, so the rounding is exactly the one stated; inputs are finite.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;            // |y| >= 448
+  if (a < 0x3C800000u) {                                // |y| < 2^-6: multiples of 2^-9
+    const float s = __uint_as_float(a) * 512.0f;        // exact
+    return sign | (uint32_t)__builtin_rintf(s);         // 0..8, nearest-even; 8 is 2^-6
+  }
+  const uint32_t mant = a & 0x7fffffu;
+  uint32_t code = (((a >> 23) - 120u) << 3) | (mant >> 20);
+  const uint32_t rem = mant & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) code += 1u;  // carry into exponent is right
+  return sign | code;                                   // never above 0x7E for |y| < 448
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 bits, nearest-even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v, int width) {
+  for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// D = A(16x128 e4m3) * B(128x16 e4m3) + C.  Lane l holds row/column l%16 and
+// K slots [32*(l/16), 32*(l/16)+32) of A/B; output element (4*(l/16)+i, l%16) in c[i].
+__device__ __forceinline__ v4f mfma16x16x128_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+}  // namespace moe355

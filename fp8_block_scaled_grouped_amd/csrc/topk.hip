@@ -1,0 +1,143 @@
+// Biased grouped top-k routing ("Accelerate DeepSeek-R1 Inference: Integrate
+// AITER into SGLang", section "Complete MoE Implementation" / "Top-K routing").
+//
+// One wave64 per token.  Scores live in LDS; the group ranking and the
+// expert selection are rounds of a wave-wide arg-best under the key
+// (value desc, index asc), so ties always go to the lower index.
+#include <limits.h>
+
+#include "device_common.h"
+#include "host_common.h"
+
+namespace moe355 {
+namespace {
+
+constexpr int kTokPerBlock = 4;
+constexpr int kMaxE = 1024;
+
+__device__ __forceinline__ bool key_better(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// Wave-wide arg-best; every lane ends with the winner.
+__device__ __forceinline__ void wave_argbest(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(i, o, kWave);
+    if (key_better(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void grouped_topk_kernel(
+    const float* __restrict__ logits, int64_t ld_logits, const float* __restrict__ bias, int T, int E,
+    int n_group, int topk_group, int topk, int renorm, float factor, float* __restrict__ topk_weights,
+    int32_t* __restrict__ topk_ids, int64_t ld_topk) {
+  __shared__ float s_sh[kTokPerBlock][kMaxE];
+  __shared__ float b_sh[kTokPerBlock][kMaxE];
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * kTokPerBlock + w;
+  const bool live = t < T;
+  const int gsz = E / n_group;
+
+  // scores: fl32 of the binary64 logistic, then the biased score in fp32
+  if (live) {
+    const float* x = logits + (int64_t)t * ld_logits;
+    for (int e = lane; e < E; e += kWave) {
+      const double d = 1.0 / (1.0 + exp(-(double)x[e]));
+      const float s = (float)d;
+      s_sh[w][e] = s;
+      b_sh[w][e] = s + bias[e];
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+
+  // group score = top1 + top2 of the biased scores; lane g owns group g
+  float gs = -INFINITY;
+  if (lane < n_group) {
+    float m1 = -INFINITY, m2 = -INFINITY;
+    const float* bg = &b_sh[w][lane * gsz];
+    for (int q = 0; q < gsz; ++q) {
+      const float v = bg[q];
+      if (v > m1) {
+        m2 = m1;
+        m1 = v;
+      } else if (v > m2) {
+        m2 = v;
+      }
+    }
+    gs = m1 + m2;
+  }
+  uint64_t gsel = 0;
+  for (int r = 0; r < topk_group; ++r) {
+    float v = (lane < n_group && !((gsel >> lane) & 1ull)) ? gs : -INFINITY;
+    int i = (lane < n_group && !((gsel >> lane) & 1ull)) ? lane : INT_MAX;
+    wave_argbest(v, i);
+    gsel |= 1ull << i;
+  }
+
+  // experts e = lane + 64*q; candidates are the experts of the kept groups
+  const int nq = (E + kWave - 1) / kWave;
+  uint32_t cand = 0;
+  for (int q = 0; q < nq; ++q) {
+    const int e = lane + kWave * q;
+    if (e < E && ((gsel >> (e / gsz)) & 1ull)) cand |= 1u << q;
+  }
+  int my_id = 0;
+  for (int j = 0; j < topk; ++j) {
+    float v = -INFINITY;
+    int i = INT_MAX;
+    for (int q = 0; q < nq; ++q) {
+      if ((cand >> q) & 1u) {
+        const int e = lane + kWave * q;
+        const float bv = b_sh[w][e];
+        if (key_better(bv, e, v, i)) {
+          v = bv;
+          i = e;
+        }
+      }
+    }
+    wave_argbest(v, i);
+    if ((i % kWave) == lane) cand &= ~(1u << (i / kWave));
+    if (lane == j) my_id = i;
+  }
+
+  // weights from the unbiased score; optional renorm (fp32, left to right); factor
+  float wv = (lane < topk) ? s_sh[w][my_id] : 0.0f;
+  if (renorm) {
+    float S = __shfl(wv, 0, kWave);
+    for (int j = 1; j < topk; ++j) S = S + __shfl(wv, j, kWave);
+    wv = wv / S;
+  }
+  wv = wv * factor;
+  if (lane < topk) {
+    topk_ids[(int64_t)t * ld_topk + lane] = my_id;
+    topk_weights[(int64_t)t * ld_topk + lane] = wv;
+  }
+}
+
+}  // namespace
+}  // namespace moe355
+
+using namespace moe355;
+
+extern "C" int grouped_topk(const float* logits, int64_t ld_logits, const float* bias, int T, int E,
+                            int n_group, int topk_group, int topk, int renorm, float routed_scaling_factor,
+                            float* topk_weights, int32_t* topk_ids, int64_t ld_topk, hipStream_t stream) {
+  MOE355_CHECK(T >= 0 && E > 0 && n_group > 0 && topk_group > 0 && topk > 0, MOE355_EINVAL);
+  MOE355_CHECK(ld_logits >= E && ld_topk >= topk, MOE355_EINVAL);
+  MOE355_CHECK(E <= kMaxE && n_group <= 64 && E % n_group == 0 && E / n_group >= 2, MOE355_EUNSUPPORTED);
+  MOE355_CHECK(topk_group <= n_group && topk <= 32 && topk <= topk_group * (E / n_group), MOE355_EUNSUPPORTED);
+  if (T == 0) return MOE355_OK;
+  MOE355_CHECK(logits && bias && topk_weights && topk_ids, MOE355_EINVAL);
+  const int blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
+  hipLaunchKernelGGL(grouped_topk_kernel, dim3(blocks), dim3(kTokPerBlock * kWave), 0, stream, logits, ld_logits,
+                     bias, T, E, n_group, topk_group, topk, renorm, routed_scaling_factor, topk_weights, topk_ids,
+                     ld_topk);
+  return launch_status();
+}

@@ -1,0 +1,271 @@
+"""Python binding of libmoe355 (ctypes).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoe355.so.  Tensors are torch CUDA (HIP) tensors; outputs are allocated
+here when not passed in, and every call is queued on torch's current stream.
+A missing library raises at the first call -- there is no fallback.
+
+Function names and argument order follow include/moe355.h.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe355.so")
+_lib = None
+
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_P64, _PSZ = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)
+
+_SIGNATURES = {
+    "moe355_strerror": ([_i32], ctypes.c_char_p),
+    "grouped_topk": ([_vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _i64, _vp], _i32),
+    "moe_sort_sizes": ([_i32, _i32, _i32, _i32, _P64, _P64, _PSZ], _i32),
+    "moe_sort": ([_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "fp8_quant_1x128": ([_vp, _i64, _i32, _i32, _vp, _i64, _vp, _i64, _i64, _vp], _i32),
+    "moe_fp8_blockscale_g1u1": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 _i64, _vp, _vp, _vp], _i32),
+    "moe_down_combine_workspace": ([_i32, _i32, _i32, _PSZ], _i32),
+    "moe_down_combine": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _vp,
+                          _i64, _vp, _sz, _vp], _i32),
+    "gemm_fp8_blockscale": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _vp], _i32),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+def lib():
+    """Load libmoe355.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmoe355.so not found at %s; build it with "
+                               "`python -m fp8_block_scaled_grouped_amd.build`" % LIB_PATH)
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = l
+    return _lib
+
+
+class Moe355Error(RuntimeError):
+    def __init__(self, code):
+        self.code = code
+        super().__init__(lib().moe355_strerror(code).decode())
+
+
+def _check(code):
+    if code != 0:
+        raise Moe355Error(code)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t
+
+
+def _rows(t, name):
+    """Row stride of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("%s must be 2-D with contiguous rows" % name)
+    return t.stride(0)
+
+
+# ----------------------------------------------------------------- routing
+def grouped_topk(logits, bias, n_group, topk_group, topk, renorm, routed_scaling_factor,
+                 topk_weights=None, topk_ids=None):
+    """Biased grouped top-k.  Returns (topk_weights fp32 [T, k], topk_ids int32 [T, k]).
+
+    Outputs may be passed in as row-strided views (same row stride for both).
+    """
+    _dev(logits, torch.float32, "logits")
+    _dev(bias, torch.float32, "bias")
+    T, E = logits.shape
+    if topk_weights is None:
+        topk_weights = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+    ld = _rows(topk_weights, "topk_weights")
+    if _rows(topk_ids, "topk_ids") != ld:
+        raise ValueError("topk_weights and topk_ids must share a row stride")
+    _check(lib().grouped_topk(_ptr(logits), _rows(logits, "logits"), _ptr(bias.contiguous()), T, E, n_group,
+                              topk_group, topk, int(bool(renorm)), float(routed_scaling_factor),
+                              _ptr(topk_weights), _ptr(topk_ids), ld, _stream()))
+    return topk_weights, topk_ids
+
+
+# ----------------------------------------------------------------- sort
+def moe_sort_sizes(T, topk, E, block_m):
+    """(max_sorted, max_blocks, workspace_bytes) -- host-only."""
+    ms, mb, ws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    _check(lib().moe_sort_sizes(T, topk, E, block_m, ctypes.byref(ms), ctypes.byref(mb), ctypes.byref(ws)))
+    return ms.value, mb.value, ws.value
+
+
+def moe_sort(topk_ids, topk_weights, E, block_m, out=None, workspace=None):
+    """Returns (sorted_ids, sorted_weights, sorted_expert_ids, num_valid) device tensors."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(topk_weights, torch.float32, "topk_weights")
+    T, k = topk_ids.shape
+    ms, mb, wsb = moe_sort_sizes(T, k, E, block_m)
+    dev = topk_ids.device
+    if out is None:
+        out = (torch.empty(ms, dtype=torch.int32, device=dev), torch.empty(ms, dtype=torch.float32, device=dev),
+               torch.empty(mb, dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    sid, sw, seid, nv = out
+    ld = _rows(topk_ids, "topk_ids")
+    if _rows(topk_weights, "topk_weights") != ld:
+        raise ValueError("topk_ids and topk_weights must share a row stride")
+    _check(lib().moe_sort(_ptr(topk_ids), _ptr(topk_weights), ld, T, k, E, block_m, _ptr(sid), _ptr(sw), _ptr(seid),
+                          _ptr(nv), _ptr(workspace), workspace.numel(), _stream()))
+    return sid, sw, seid, nv
+
+
+# ----------------------------------------------------------------- quant
+def fp8_quant_1x128(x, q=None, scale=None, scale_layout="row"):
+    """bf16 [M, K] -> (e4m3 uint8 [M, K], fp32 scales).
+
+    scale_layout "row": scales [M, K/128]; "kblock": scales [K/128, M].
+    """
+    _dev(x, torch.bfloat16, "x")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        shape = (M, K // 128) if scale_layout == "row" else (K // 128, M)
+        scale = torch.empty(shape, dtype=torch.float32, device=x.device)
+    ssm, sskb = (K // 128, 1) if scale_layout == "row" else (1, M)
+    _check(lib().fp8_quant_1x128(_ptr(x), _rows(x, "x"), M, K, _ptr(q), _rows(q, "q"), _ptr(scale), ssm, sskb,
+                                 _stream()))
+    return q, scale
+
+
+def _scale_strides(a_scale, T, H, scale_layout):
+    if scale_layout == "row":
+        assert a_scale.shape == (T, H // 128)
+        return H // 128, 1
+    assert a_scale.shape == (H // 128, T)
+    return 1, T
+
+
+# ----------------------------------------------------------------- grouped GEMMs
+def moe_fp8_blockscale_g1u1(a8, a_scale, w1, w1_scale, sorted_ids, sorted_expert_ids, num_valid, topk, block_m,
+                            h8=None, h_scale=None, scale_layout="row"):
+    """Gate/up grouped GEMM + SiLU*up + 1x128 requant.  Returns (h8 [max_sorted, I], h_scale [max_sorted, I/128])."""
+    _dev(a8, torch.uint8, "a8")
+    _dev(w1, torch.uint8, "w1")
+    T, H = a8.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    ms = sorted_ids.numel()
+    if h8 is None:
+        h8 = torch.empty((ms, I), dtype=torch.uint8, device=a8.device)
+    if h_scale is None:
+        h_scale = torch.empty((ms, I // 128), dtype=torch.float32, device=a8.device)
+    ssm, sskb = _scale_strides(a_scale, T, H, scale_layout)
+    _check(lib().moe_fp8_blockscale_g1u1(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(w1), _ptr(w1_scale),
+                                         _ptr(sorted_ids), _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E,
+                                         topk, block_m, ms, _ptr(h8), _ptr(h_scale), _stream()))
+    return h8, h_scale
+
+
+def moe_down_combine_workspace(T, H, topk):
+    b = ctypes.c_size_t()
+    _check(lib().moe_down_combine_workspace(T, H, topk, ctypes.byref(b)))
+    return b.value
+
+
+def moe_down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sorted_expert_ids, num_valid, T, topk,
+                     block_m, out=None, workspace=None):
+    """Down grouped GEMM + top-k weighted combine.  Returns bf16 [T, H]."""
+    _dev(h8, torch.uint8, "h8")
+    _dev(w2, torch.uint8, "w2")
+    E, H, I = w2.shape
+    ms = sorted_ids.numel()
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=h8.device)
+    if workspace is None:
+        workspace = torch.empty(moe_down_combine_workspace(T, H, topk), dtype=torch.uint8, device=h8.device)
+    _check(lib().moe_down_combine(_ptr(h8), _ptr(h_scale), _ptr(w2), _ptr(w2_scale), _ptr(sorted_ids),
+                                  _ptr(sorted_weights), _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E, topk,
+                                  block_m, ms, _ptr(out), _rows(out, "out"), _ptr(workspace), workspace.numel(),
+                                  _stream()))
+    return out
+
+
+# ----------------------------------------------------------------- dense
+def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row"):
+    """a8 e4m3 [M, K] (1x128 scales), b8 e4m3 [N, K] (128x128 scales) -> bf16 [M, N]."""
+    _dev(a8, torch.uint8, "a8")
+    _dev(b8, torch.uint8, "b8")
+    M, K = a8.shape
+    N = b8.shape[0]
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a8.device)
+    ssm, sskb = _scale_strides(a_scale, M, K, scale_layout)
+    _check(lib().gemm_fp8_blockscale(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(b8), _ptr(b_scale), M, N, K, _ptr(c),
+                                     _rows(c, "c"), _stream()))
+    return c
+
+
+# ----------------------------------------------------------------- the layer
+class MoELayer:
+    """The five calls of one MoE layer on preallocated buffers (no allocation per call).
+
+    forward(hidden bf16 [T, H], logits fp32 [T, E]) -> bf16 [T, H], running
+    grouped_topk -> moe_sort -> fp8_quant_1x128 -> moe_fp8_blockscale_g1u1 ->
+    moe_down_combine on the current stream.
+    """
+
+    def __init__(self, cfg, bias, w1, w1_scale, w2, w2_scale, T=None, block_m=None, scale_layout="row"):
+        self.cfg = cfg
+        self.T = cfg.T if T is None else T
+        self.block_m = cfg.block_m if block_m is None else block_m
+        self.bias, self.w1, self.w1_scale, self.w2, self.w2_scale = bias, w1, w1_scale, w2, w2_scale
+        self.scale_layout = scale_layout
+        dev = w1.device
+        T, H, I, E, k = self.T, cfg.H, cfg.I, cfg.E, cfg.topk
+        ms, mb, wsb = moe_sort_sizes(T, k, E, self.block_m)
+        self.max_sorted = ms
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.sort_out = (torch.empty(ms, dtype=torch.int32, device=dev), torch.empty(ms, dtype=torch.float32,
+                                                                                      device=dev),
+                         torch.empty(mb, dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32,
+                                                                                      device=dev))
+        self.sort_ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        self.a8 = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        self.a_scale = torch.empty((T, H // 128) if scale_layout == "row" else (H // 128, T), dtype=torch.float32,
+                                   device=dev)
+        self.h8 = torch.empty((ms, I), dtype=torch.uint8, device=dev)
+        self.h_scale = torch.empty((ms, I // 128), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.down_ws = torch.empty(moe_down_combine_workspace(T, H, k), dtype=torch.uint8, device=dev)
+
+    def forward(self, hidden, logits):
+        c = self.cfg
+        grouped_topk(logits, self.bias, c.n_group, c.topk_group, c.topk, c.renorm, c.routed_scaling_factor,
+                     self.topk_w, self.topk_ids)
+        sid, sw, seid, nv = moe_sort(self.topk_ids, self.topk_w, c.E, self.block_m, self.sort_out, self.sort_ws)
+        fp8_quant_1x128(hidden, self.a8, self.a_scale, self.scale_layout)
+        moe_fp8_blockscale_g1u1(self.a8, self.a_scale, self.w1, self.w1_scale, sid, seid, nv, c.topk, self.block_m,
+                                self.h8, self.h_scale, self.scale_layout)
+        moe_down_combine(self.h8, self.h_scale, self.w2, self.w2_scale, sid, sw, seid, nv, self.T, c.topk,
+                         self.block_m, self.out, self.down_ws)
+        return self.out

@@ -1,0 +1,87 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented codes before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe355.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", txt, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from fp8_block_scaled_grouped_amd import moe355
+    if not os.path.exists(moe355.LIB_PATH):
+        pytest.skip("libmoe355.so not built")
+    return moe355.lib()
+
+
+def test_header_declares_the_six_calls():
+    d = _declared()
+    for name in ["grouped_topk", "moe_sort", "fp8_quant_1x128", "moe_fp8_blockscale_g1u1", "moe_down_combine",
+                 "gemm_fp8_blockscale", "moe_sort_sizes", "moe_down_combine_workspace", "moe355_strerror"]:
+        assert name in d, name
+
+
+def test_every_declared_symbol_exported(lib):
+    from fp8_block_scaled_grouped_amd import moe355
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert name in moe355.EXPORTED, name
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -99):
+        assert lib.moe355_strerror(code).decode().startswith("moe355:")
+
+
+def test_sort_sizes(lib):
+    from fp8_block_scaled_grouped_amd import moe355
+    import oracle
+    for T, k, E, BM in [(16, 4, 16, 16), (64, 8, 256, 16), (8192, 8, 256, 128), (4096, 8, 256, 64), (0, 8, 256, 32)]:
+        ms, mb, ws = moe355.moe_sort_sizes(T, k, E, BM)
+        assert (ms, mb) == oracle.sort.max_sizes(T, k, E, BM)
+        assert ws > 0
+    with pytest.raises(moe355.Moe355Error) as e:
+        moe355.moe_sort_sizes(16, 4, 16, 48)
+    assert e.value.code == -2
+
+
+def _p(v=16):
+    return ctypes.c_void_p(v)
+
+
+def test_invalid_arguments_return_codes(lib):
+    L = lib
+    # grouped_topk: E % n_group != 0 -> EUNSUPPORTED; ld_topk < topk -> EINVAL; null -> EINVAL
+    assert L.grouped_topk(_p(), 16, _p(), 4, 16, 3, 2, 4, 1, 1.0, _p(), _p(), 4, None) == -2
+    assert L.grouped_topk(_p(), 16, _p(), 4, 16, 4, 2, 4, 1, 1.0, _p(), _p(), 3, None) == -1
+    assert L.grouped_topk(None, 16, _p(), 4, 16, 4, 2, 4, 1, 1.0, _p(), _p(), 4, None) == -1
+    assert L.grouped_topk(_p(), 16, _p(), 4, 16, 4, 2, 9, 1, 1.0, _p(), _p(), 9, None) == -2   # topk > tg*E/G
+    assert L.grouped_topk(_p(), 16, _p(), 0, 16, 4, 2, 4, 1, 1.0, None, None, 4, None) == 0    # T = 0 no-op
+    # quant: K % 128 -> EUNSUPPORTED; misaligned -> EMISALIGNED; ld < K -> EINVAL
+    assert L.fp8_quant_1x128(_p(), 200, 4, 200, _p(), 200, _p(), 2, 1, None) == -2
+    assert L.fp8_quant_1x128(_p(8), 256, 4, 256, _p(), 256, _p(), 2, 1, None) == -3
+    assert L.fp8_quant_1x128(_p(), 128, 4, 256, _p(), 256, _p(), 2, 1, None) == -1
+    # dense GEMM: N % 128 -> EUNSUPPORTED; ldc < N -> EINVAL
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 100, 256, _p(), 100, None) == -2
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 64, None) == -1
+    # sort: workspace too small -> EINVAL; bad block_m -> EUNSUPPORTED
+    assert L.moe_sort(_p(), _p(), 4, 16, 4, 16, 16, _p(), _p(), _p(), _p(), _p(), 1, None) == -1
+    assert L.moe_sort(_p(), _p(), 4, 16, 4, 16, 24, _p(), _p(), _p(), _p(), _p(), 1 << 20, None) == -2
+    # g1u1: capacity below the worst case -> EINVAL; I % 128 -> EUNSUPPORTED
+    assert L.moe_fp8_blockscale_g1u1(_p(), _p(), 2, 1, _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16, 100,
+                                     _p(), _p(), None) == -1
+    assert L.moe_fp8_blockscale_g1u1(_p(), _p(), 2, 1, _p(), _p(), _p(), _p(), _p(), 16, 256, 100, 16, 4, 16, 304,
+                                     _p(), _p(), None) == -2
+    # down: workspace too small
+    assert L.moe_down_combine(_p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16, 304, _p(),
+                              256, _p(), 8, None) == -1

@@ -1,0 +1,226 @@
+"""GPU parity on the tiny MoE layer and small dense shapes (every output element checked)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8 as ofp8
+from tests.helpers import assert_rel_max, check_requant, f32_of_bf16, np_u8, oracle_routing
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def m():
+    import fp8_block_scaled_grouped_amd as mod
+    mod.lib()
+    return mod
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    from fp8_block_scaled_grouped_amd import inputs
+    cfg = inputs.MOE_CONFIGS["tiny"]
+    return cfg, inputs.make_moe_inputs(cfg, "cpu", seed=0)
+
+
+def _edge_rows(K):
+    rows = [np.zeros(K), -np.zeros(K), np.linspace(-3, 3, K), np.full(K, 1e-30), np.full(K, -2.0 ** -140)]
+    v = ofp8.decode(np.arange(127, dtype=np.uint8))
+    mids = ((v[:-1] + v[1:]) / 2)
+    rows.append(np.resize(np.concatenate([mids, -mids, [448.0]]), K))   # exact midpoints, amax 448
+    rows.append(np.resize(np.array([1e30, -1e30, 3e38, 1.0]), K))
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("M,K", [(16, 256), (37, 1280), (1, 128), (300, 7168)])
+@pytest.mark.parametrize("layout", ["row", "kblock"])
+def test_quant_bitexact(m, M, K, layout):
+    print("quant", M, K, layout, flush=True)
+    g = torch.Generator().manual_seed(M * 131 + K)
+    x = (torch.randn((M, K), generator=g) * torch.exp2(torch.randint(-30, 30, (M, 1), generator=g).float()))
+    x = x.to(torch.bfloat16)
+    if M >= 7:
+        x[:7] = torch.from_numpy(_edge_rows(K)).to(torch.bfloat16)
+    q, s = m.fp8_quant_1x128(x.to(DEV), scale_layout=layout)
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant.quant_1x128(f32_of_bf16(x))
+    s = s.cpu().numpy()
+    if layout == "kblock":
+        s = s.T
+    assert np.array_equal(np_u8(q), qr)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+
+
+def test_quant_strided_rows(m):
+    x = torch.randn((8, 512 + 64)).to(torch.bfloat16).to(DEV)[:, :512]
+    qbuf = torch.zeros((8, 640), dtype=torch.uint8, device=DEV)
+    q, s = m.fp8_quant_1x128(x, q=qbuf[:, :512])
+    torch.cuda.synchronize()
+    qr, sr = oracle.quant.quant_1x128(f32_of_bf16(x))
+    assert np.array_equal(np_u8(qbuf[:, :512]), qr) and np.all(np_u8(qbuf[:, 512:]) == 0)
+    assert np.array_equal(s.cpu().numpy(), sr)
+
+
+@pytest.mark.parametrize("ld_extra", [0, 10])
+def test_topk_bitexact_tiny(m, tiny, ld_extra):
+    cfg, x = tiny
+    k = cfg.topk
+    wbuf = torch.full((cfg.T, k + ld_extra), -7.0, device=DEV)
+    ibuf = torch.full((cfg.T, k + ld_extra), -7, dtype=torch.int32, device=DEV)
+    m.grouped_topk(x["logits"].to(DEV), x["bias"].to(DEV), cfg.n_group, cfg.topk_group, k, cfg.renorm,
+                   cfg.routed_scaling_factor, wbuf[:, :k], ibuf[:, :k])
+    torch.cuda.synchronize()
+    w, ids = oracle_routing(x, cfg)
+    assert np.array_equal(ibuf[:, :k].cpu().numpy(), ids)
+    assert np.array_equal(wbuf[:, :k].cpu().numpy().view(np.uint32), w.view(np.uint32))
+    assert np.all(ibuf[:, k:].cpu().numpy() == -7)
+
+
+@pytest.mark.parametrize("T,E,G,tg,k,renorm", [(1, 16, 4, 2, 4, True), (33, 64, 8, 3, 6, False), (5, 1024, 64, 8, 32, True),
+                                               (100, 256, 8, 4, 8, True), (7, 24, 3, 2, 5, True)])
+def test_topk_bitexact_shapes(m, T, E, G, tg, k, renorm):
+    g = torch.Generator().manual_seed(T * 7 + E)
+    logits = torch.randn((T, E), generator=g)
+    bias = torch.randn((E,), generator=g) * 0.1
+    w, ids = m.grouped_topk(logits.to(DEV), bias.to(DEV), G, tg, k, renorm, 2.5)
+    torch.cuda.synchronize()
+    wr, ir = oracle.routing.grouped_topk(logits.numpy(), bias.numpy(), G, tg, k, renorm, 2.5)
+    assert np.array_equal(ids.cpu().numpy(), ir)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), wr.view(np.uint32))
+
+
+def test_topk_ties(m):
+    logits = torch.zeros((3, 16))
+    logits[1, ::2] = 1.0
+    logits[2] = torch.tensor([1.0, 1.0, 0, 0] * 4)
+    w, ids = m.grouped_topk(logits.to(DEV), torch.zeros(16, device=DEV), 4, 2, 4, True, 1.0)
+    torch.cuda.synchronize()
+    wr, ir = oracle.routing.grouped_topk(logits.numpy(), np.zeros(16, np.float32), 4, 2, 4, True, 1.0)
+    assert np.array_equal(ids.cpu().numpy(), ir)
+    assert np.array_equal(w.cpu().numpy(), wr)
+
+
+def _check_sort(m, ids, w, E, BM, ld_extra=0):
+    T, k = ids.shape
+    ib = torch.zeros((T, k + ld_extra), dtype=torch.int32)
+    wb = torch.zeros((T, k + ld_extra), dtype=torch.float32)
+    ib[:, :k] = torch.from_numpy(ids)
+    wb[:, :k] = torch.from_numpy(w)
+    ib, wb = ib.to(DEV), wb.to(DEV)
+    sid, sw, seid, nv = m.moe_sort(ib[:, :k], wb[:, :k], E, BM)
+    torch.cuda.synchronize()
+    rsid, rsw, rseid, P = oracle.sort.moe_sort(ids, w, E, BM)
+    assert int(nv.item()) == P
+    assert np.array_equal(sid.cpu().numpy()[:P], rsid)
+    assert np.array_equal(sw.cpu().numpy()[:P].view(np.uint32), rsw.view(np.uint32))
+    assert np.array_equal(seid.cpu().numpy()[:P // BM], rseid)
+
+
+@pytest.mark.parametrize("BM", [16, 32, 64, 128])
+def test_sort_bitexact_tiny_routing(m, tiny, BM):
+    cfg, x = tiny
+    w, ids = oracle_routing(x, cfg)
+    _check_sort(m, ids, w, cfg.E, BM, ld_extra=10)
+
+
+@pytest.mark.parametrize("T,k,E,BM", [(1, 1, 4, 16), (1000, 8, 256, 64), (300, 3, 1024, 16), (4096, 8, 256, 128)])
+def test_sort_bitexact_random(m, T, k, E, BM):
+    rng = np.random.default_rng(T + E)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    _check_sort(m, ids, w, E, BM)
+
+
+def test_sort_all_one_expert_and_skewed(m):
+    T, k, E = 777, 2, 32
+    ids = np.stack([np.full(T, 5), np.full(T, 6)], 1).astype(np.int32)
+    _check_sort(m, ids, np.ones((T, k), np.float32), E, 128)
+    rng = np.random.default_rng(3)
+    hot = rng.random((T, 4)) < 0.9
+    ids = np.where(hot, np.arange(4)[None, :], rng.integers(4, E, (T, 4))).astype(np.int32)
+    ids = np.stack([rng.permutation(E)[:4] if len(set(r)) < 4 else r for r in ids]).astype(np.int32)
+    _check_sort(m, ids, rng.random((T, 4)).astype(np.float32), E, 64)
+
+
+def _tiny_stage_inputs(tiny, BM):
+    cfg, x = tiny
+    w, ids = oracle_routing(x, cfg)
+    sid, sw, seid, P = oracle.sort.moe_sort(ids, w, cfg.E, BM)
+    ms = oracle.sort.max_sizes(cfg.T, cfg.topk, cfg.E, BM)[0]
+    pad = lambda a, fill: np.concatenate([a, np.full(ms - len(a), fill, a.dtype)])
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(x["hidden"]))
+    return cfg, x, w, ids, (pad(sid, cfg.T * cfg.topk), pad(sw, np.float32(0)), pad(seid, 0), P), a8, sa
+
+
+@pytest.mark.parametrize("BM", [16, 32, 64, 128])
+def test_g1u1_stage_tiny(m, tiny, BM):
+    cfg, x, w, ids, (sid, sw, seid, P), a8, sa = _tiny_stage_inputs(tiny, BM)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    h8, hs = m.moe_fp8_blockscale_g1u1(t(a8), t(sa), x["w1"].to(DEV), x["w1_scale"].to(DEV), t(sid), t(seid),
+                                       t(np.array([P], np.int32)), cfg.topk, BM)
+    torch.cuda.synchronize()
+    _, _, h_ref, valid = oracle.moe.g1u1(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), sid, seid, P, cfg.topk, BM)
+    rows = np.nonzero(valid)[0]
+    check_requant(np_u8(h8)[rows], hs.cpu().numpy()[rows], h_ref[rows])
+
+
+@pytest.mark.parametrize("BM", [16, 64])
+def test_down_stage_tiny(m, tiny, BM):
+    cfg, x, w, ids, (sid, sw, seid, P), a8, sa = _tiny_stage_inputs(tiny, BM)
+    h8, hs, _, valid = oracle.moe.g1u1(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), sid, seid, P, cfg.topk, BM)
+    ms = len(sid)
+    h8p = np.zeros((ms, cfg.I), np.uint8)
+    hsp = np.ones((ms, cfg.I // 128), np.float32)
+    h8p[:P], hsp[:P] = h8, hs
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    out = m.moe_down_combine(t(h8p), t(hsp), x["w2"].to(DEV), x["w2_scale"].to(DEV), t(sid), t(sw), t(seid),
+                             t(np.array([P], np.int32)), cfg.T, cfg.topk, BM)
+    torch.cuda.synchronize()
+    ref = oracle.moe.down_combine(h8, hs, x["w2"].numpy(), x["w2_scale"].numpy(), sid, sw, seid, P, cfg.T, cfg.topk, BM)
+    assert_rel_max(f32_of_bf16(out), ref, what="down_combine tiny")
+    # also tight: bf16 rounding of an fp32 sum
+    assert np.all(np.abs(f32_of_bf16(out) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("BM", [16, 32])
+@pytest.mark.parametrize("layout", ["row", "kblock"])
+def test_layer_tiny(m, tiny, BM, layout):
+    cfg, x = tiny
+    g = {k: v.to(DEV) for k, v in x.items()}
+    layer = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"], block_m=BM,
+                       scale_layout=layout)
+    out = layer.forward(g["hidden"], g["logits"])
+    torch.cuda.synchronize()
+    w, ids = oracle_routing(x, cfg)
+    assert np.array_equal(layer.topk_ids.cpu().numpy(), ids)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(x["hidden"]))
+    ref, _, _ = oracle.moe.layer_tokens(np.arange(cfg.T), a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(),
+                                        x["w2"].numpy(), x["w2_scale"].numpy(), ids, w)
+    assert_rel_max(f32_of_bf16(out), ref, what="tiny layer")
+
+
+def test_layer_tiny_deterministic(m, tiny):
+    cfg, x = tiny
+    g = {k: v.to(DEV) for k, v in x.items()}
+    layer = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"])
+    a = layer.forward(g["hidden"], g["logits"]).clone()
+    b = layer.forward(g["hidden"], g["logits"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 384, 512), (37, 384, 512), (128, 256, 1024), (200, 128, 256), (16, 2048, 7168)])
+@pytest.mark.parametrize("layout", ["row", "kblock"])
+def test_dense_small(m, M, N, K, layout):
+    from fp8_block_scaled_grouped_amd import inputs
+    d = inputs.make_dense_inputs(M, N, K, "cpu", seed=M + N)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(d["a"]))
+    sa_dev = torch.from_numpy(sa if layout == "row" else np.ascontiguousarray(sa.T)).to(DEV)
+    c = m.gemm_fp8_blockscale(torch.from_numpy(a8).to(DEV), sa_dev, d["b"].to(DEV), d["b_scale"].to(DEV),
+                              scale_layout=layout)
+    torch.cuda.synchronize()
+    ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
+    assert_rel_max(f32_of_bf16(c), ref, what="dense %dx%dx%d" % (M, N, K))
