@@ -96,7 +96,7 @@ def cpu_baseline_moe(cfg, hidden, logits, bias, w1, s1, w2, s2, budget_s):
             W1[e], W2[e]
         t0 = time.perf_counter()
         a8, sa = oracle.quant.quant_1x128(hid[done:done + 1])
-        oracle.moe.layer_tokens(np.arange(1), a8, sa, W1, s1, W2, s2, ids[done:done + 1], w[done:done + 1])
+        oracle.moe.layer_tokens(a8, sa, W1, s1, W2, s2, ids[done:done + 1], w[done:done + 1])
         el += time.perf_counter() - t0
         done += 1
     sec = el + t_route * done / cfg.T

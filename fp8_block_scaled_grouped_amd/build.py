@@ -17,6 +17,9 @@ LIB = os.path.join(PKG, "libmoe355.so")
 SOURCES = ["topk.hip", "sort.hip", "quant.hip", "gemm.hip", "status.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# per-source extra flags: MFMA results in VGPRs so the fp32 fold reads them directly
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms stay off: plain scalar fp32 arithmetic only
@@ -32,7 +35,7 @@ def build(save_temps=None, verbose=False):
         path = os.path.join(CSRC, src)
         obj = os.path.join(CSRC, "_obj", src + ".o")
         os.makedirs(os.path.dirname(obj), exist_ok=True)
-        cmd = [HIPCC] + HIP_FLAGS + ["-c", path, "-o", obj]
+        cmd = [HIPCC] + HIP_FLAGS + EXTRA.get(src, []) + ["-c", path, "-o", obj]
         if src.endswith(".cpp"):
             cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-c", path, "-o", obj]
         if save_temps and src.endswith(".hip"):

@@ -20,16 +20,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   const uint32_t u = __float_as_uint(y);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7fffffffu;
-  if (a >= 0x43E00000u) return sign | 0x7Eu;            // |y| >= 448
-  if (a < 0x3C800000u) {                                // |y| < 2^-6: multiples of 2^-9
-    const float s = __uint_as_float(a) * 512.0f;        // exact
-    return sign | (uint32_t)__builtin_rintf(s);         // 0..8, nearest-even; 8 is 2^-6
-  }
+  // |y| < 2^-6: multiples of 2^-9, nearest-even (8 encodes 2^-6 itself)
+  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(a < 0x3C800000u ? a : 0x3C800000u) * 512.0f);
+  // normal range: keep 3 mantissa bits, nearest-even on the 20 dropped bits
   const uint32_t mant = a & 0x7fffffu;
   uint32_t code = (((a >> 23) - 120u) << 3) | (mant >> 20);
   const uint32_t rem = mant & 0xfffffu;
-  if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) code += 1u;  // carry into exponent is right
-  return sign | code;                                   // never above 0x7E for |y| < 448
+  code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;  // carry into exponent is right
+  uint32_t r = a < 0x3C800000u ? sub : code;
+  r = a >= 0x43E00000u ? 0x7Eu : r;  // |y| >= 448 saturates
+  return sign | r;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }

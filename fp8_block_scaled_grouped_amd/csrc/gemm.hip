@@ -1,23 +1,30 @@
 // Block-scaled FP8 GEMM engine on gfx950 FP8 MFMA.
 //
-// One workgroup (4 waves) computes a BM x 128 output tile; the K loop walks
-// 128-wide scale blocks.  Per block each wave runs 16x16x128 FP8 MFMAs into a
-// fresh fp32 tile and folds it into its accumulators as acc += tile *
-// (a_scale(row) * b_scale), so both scales are applied once per 128 of K in
-// fp32 ("Accelerate DeepSeek-R1 Inference: Integrate AITER into SGLang",
-// section "General Linear Layer": 1x128 activation scales, 128x128 weight
-// scales).  A and B tiles are staged through LDS, double buffered, with
-// 16-byte global loads and an XOR swizzle of the 16-byte chunks of each row.
+// Each workgroup computes a BM x BNB tile of A[rows, K] * B[BNB rows, K]^T
+// ("Accelerate DeepSeek-R1 Inference: Integrate AITER into SGLang", section
+// "General Linear Layer": one activation scale per 1x128, one weight scale
+// per 128x128).  The K loop walks 128-wide scale blocks.  Per block each wave
+// runs 16x16x128 FP8 MFMAs into fresh fp32 tiles and folds every tile into
+// its accumulators as acc += tile * (a_scale(row) * b_scale) two MFMAs after
+// issuing it, so the fold overlaps the matrix pipe.
+//
+// Data movement: A and B tiles (and the per-row A scales) go HBM -> LDS by
+// LDS-DMA (global_load_lds), S stages deep, with no VGPR staging.  Rows are
+// 128 bytes in LDS with the 16-byte chunk c of row r stored in slot
+// c ^ ((r >> 1) & 7): the 16 lanes that read one chunk of 16 consecutive rows
+// hit 16 different bank groups.  Each wave waits for its own DMAs with
+// s_waitcnt vmcnt and a bare s_barrier publishes the stage.
 //
 // Modes:
-//   dense  C[M, N] = A[M, K] * B[N, K]^T, bf16 out ("General Linear Layer").
-//   g1u1   grouped GEMM over the sorted pairs ("Complete MoE Implementation" /
-//          "Blockscale FP8 MoE Computation"): A rows gathered through
-//          sorted_ids, B = gate and up rows of the block's expert, epilogue
-//          h = SiLU(gate) * up and 1x128 e4m3 requantisation of h.
-//   down   grouped GEMM of h with the expert's down weights; each row is scaled
-//          by its routing weight and staged per flat pair; a second kernel sums
-//          each token's pairs in ascending order into bf16.
+//   dense  C[M, N] = A[M, K] B[N, K]^T, bf16 out ("General Linear Layer").
+//   g1u1   grouped GEMM over the sorted token-expert pairs ("Complete MoE
+//          Implementation" / "Blockscale FP8 MoE Computation"): A rows
+//          gathered through sorted_ids, B = 128 gate rows and the matching 128
+//          up rows of the block's expert; epilogue h = SiLU(gate) * up and a
+//          1x128 e4m3 requantisation of h.
+//   down   grouped GEMM of h with the expert's down weights; each row is
+//          scaled by its routing weight and staged per flat pair; a second
+//          kernel sums each token's pairs in ascending order into bf16.
 #include "device_common.h"
 #include "host_common.h"
 
@@ -47,277 +54,331 @@ struct GemmArgs {
   float* y;                // down staging [T*topk, N] fp32
 };
 
-template <int BM, int MODE>
-struct Tile {
-  static constexpr int kParts = MODE == kG1U1 ? 2 : 1;  // g1u1: gate and up
-  static constexpr int kBRows = 128 * kParts;
-  static constexpr int kWM = BM >= 64 ? 2 : 1;            // waves along M
-  static constexpr int kWN = 4 / kWM;                      // waves along N
-  static constexpr int kWTM = BM / kWM;                    // rows per wave
-  static constexpr int kWTN = 128 / kWN;                   // output columns per wave
+// Tile configuration.  BNB = B rows staged per workgroup (g1u1: 128 gate + 128 up).
+template <int MODE, int BM_, int BNB_, int NW_, int WM_, int S_>
+struct Cfg {
+  static constexpr int BM = BM_, BNB = BNB_, NW = NW_, WM = WM_, S = S_;
+  static constexpr int kThreads = NW * 64;
+  static constexpr int kWN = NW / WM;
+  static constexpr int kParts = MODE == kG1U1 ? 2 : 1;
+  static constexpr int kOutN = BNB / kParts;          // output columns per workgroup
+  static constexpr int kWTM = BM / WM;                // rows per wave
+  static constexpr int kWTNB = BNB / kWN;             // B rows per wave (inside one part)
   static constexpr int kTM = kWTM / 16;
-  static constexpr int kTN = kWTN / 16;
-  static constexpr int kAChunks = BM * 8;
-  static constexpr int kAPerThread = (kAChunks + 255) / 256;
-  static constexpr int kBPerThread = kBRows * 8 / 256;
+  static constexpr int kTN = kWTNB / 16;
+  static constexpr int kAQ0 = BM / 8;                 // 1 KB DMA rows-of-8 for A
+  static constexpr int kBQ = BNB / 8;
+  static constexpr int kAQ = (kAQ0 + kBQ + NW - 1) / NW * NW - kBQ;  // padded: every wave issues the same count
+  static constexpr int kQW = (kAQ + kBQ) / NW;        // 16-byte DMAs per lane per stage
+  static constexpr int kLoadsPerStage = kQW + 1;      // + the wave's A-scale DMA
+  static constexpr int kAOff = 0;
+  static constexpr int kBOff = kAQ * 1024;
+  static constexpr int kSOff = kBOff + kBQ * 1024;
+  static constexpr int kStage = kSOff + NW * 256;     // 64 fp32 A scales per wave
+  static constexpr int kLds = S * kStage;
+  static_assert(kWTM % 16 == 0 && kWTNB % 16 == 0, "wave tile must be whole MFMA tiles");
+  static_assert(kWTNB <= 128 && 128 % kWTNB == 0, "a wave's columns lie in one 128-column scale block");
+  static_assert(kWTM <= 64, "one A-scale DMA per wave covers 64 rows");
+  static_assert(MODE != kG1U1 || BNB == 256, "g1u1 stages 128 gate and 128 up rows");
+  static_assert(kWN % kParts == 0, "gate and up waves split evenly");
+  static_assert(S >= 2 && S <= 4 && 2 * kLoadsPerStage < 64, "pipeline depth");
 };
 
-__device__ __forceinline__ int swz(int r, int ch) { return r * 128 + ((ch ^ (r & 7)) << 4); }
+__device__ __forceinline__ int swz(int r, int ch) { return r * 128 + ((ch ^ ((r >> 1) & 7)) << 4); }
 
-// MFMA operand of row r: K slots [32g, 32g+32) are chunks 2g and 2g+1.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS-DMA: every lane moves 16 (or 4) bytes from its global address to
+// LDS[m0 + 16*lane] (or 4*lane).  Issued from asm so that the compiler does not
+// drain the DMA queue before each LDS read; completion is tracked explicitly
+// with vm_wait.  No output registers.
+__device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// wait until at most a*PER of this wave's DMAs are in flight, a in [0, 2]
+template <int PER>
+__device__ __forceinline__ void vm_wait_stages(int a) {
+  if (a >= 2) {
+    vm_wait<2 * PER>();
+  } else if (a == 1) {
+    vm_wait<PER>();
+  } else {
+    vm_wait<0>();
+  }
+}
+
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// MFMA operand of tile row r: K slots [32g, 32g+32) are chunks 2g and 2g+1.
 __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int g) {
   const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + swz(r, 2 * g));
   const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + swz(r, 2 * g + 1));
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// Global -> registers for one K step: 16-byte chunks of the A and B tiles.
-template <int NA, int NB>
-__device__ __forceinline__ void gload_tile(u32x4 (&ra)[NA], u32x4 (&rb)[NB], const uint8_t* const (&a_src)[NA],
-                                           const uint8_t* const (&b_src)[NB], bool a_live, int64_t koff) {
-#pragma unroll
-  for (int i = 0; i < NA; ++i)
-    if (i + 1 < NA || a_live) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + koff);
-#pragma unroll
-  for (int i = 0; i < NB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + koff);
-}
+template <class C, int MODE>
+__global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLds];
+  __shared__ int rowinfo[C::BM];
+  __shared__ float red[C::kWN][C::BM];
 
-// Registers -> LDS (swizzled offsets precomputed per thread).
-template <int NA, int NB>
-__device__ __forceinline__ void lstore_tile(uint8_t* a_tile, uint8_t* b_tile, const u32x4 (&ra)[NA],
-                                            const u32x4 (&rb)[NB], const int (&a_off)[NA], const int (&b_off)[NB],
-                                            bool a_live) {
-#pragma unroll
-  for (int i = 0; i < NA; ++i)
-    if (i + 1 < NA || a_live) *reinterpret_cast<u32x4*>(a_tile + a_off[i]) = ra[i];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4*>(b_tile + b_off[i]) = rb[i];
-}
-
-template <int BM, int MODE>
-__global__ __launch_bounds__(256) void bs_gemm_kernel(GemmArgs g) {
-  using C = Tile<BM, MODE>;
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][BM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t b_lds[2][C::kBRows * 128];
-  __shared__ __attribute__((aligned(16))) float sa_lds[2][BM];
-  __shared__ int rowinfo[BM];
-  __shared__ float red[C::kWN][BM];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::kWN, wn = wave % C::kWN;
-  const int NT = g.N / 128;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in SGPRs
+  const int wm = w / C::kWN, wn = w % C::kWN;
+  const int NT = g.N / C::kOutN;
   const int nt = (int)(blockIdx.x % NT);
   const int mb = (int)(blockIdx.x / NT);
-  const int64_t row0 = (int64_t)mb * BM;
+  const int64_t row0 = (int64_t)mb * C::BM;
   const int KB = g.K / 128;
   const int npairs = g.T * g.topk;
 
   int expert = 0, nvalid = 0;
   if constexpr (MODE != kDense) {
     nvalid = g.num_valid[0];
-    if (row0 >= nvalid) return;  // uniform: this block holds no sorted rows
+    if (row0 >= nvalid) return;  // uniform: no sorted rows in this block
     expert = g.sorted_eids[mb];
-    if (tid < BM) rowinfo[tid] = g.sorted_ids[row0 + tid];
+    for (int i = tid; i < C::BM; i += C::kThreads) rowinfo[i] = g.sorted_ids[row0 + i];
     __syncthreads();
   }
 
-  // ---- per-thread global sources (advance by 128 bytes per K step)
-  const uint8_t* a_src[C::kAPerThread];
-  int a_off[C::kAPerThread];
-#pragma unroll
-  for (int i = 0; i < C::kAPerThread; ++i) {
-    const int ci = tid + 256 * i;
-    const int r = (ci >> 3) < BM ? (ci >> 3) : BM - 1;
-    const int ch = ci & 7;
-    int64_t arow;
+  // global row of A-tile row r
+  auto a_row = [&](int r) -> int64_t {
     if constexpr (MODE == kDense) {
-      arow = row0 + r < g.M ? row0 + r : g.M - 1;
+      return row0 + r < g.M ? row0 + r : g.M - 1;
     } else if constexpr (MODE == kG1U1) {
       const int pid = rowinfo[r];
-      arow = pid < npairs ? pid / g.topk : 0;
+      return pid < npairs ? pid / g.topk : 0;
     } else {
-      arow = row0 + r;
+      return row0 + r;
     }
-    a_src[i] = g.a + arow * g.K + ch * 16;
-    a_off[i] = swz(r, ch);
-  }
-  const float* sa_src = g.a_scale;
-  if (tid < BM) {
-    int64_t arow;
+  };
+  // global row of B-tile row r
+  auto b_row = [&](int r) -> int64_t {
     if constexpr (MODE == kDense) {
-      arow = row0 + tid < g.M ? row0 + tid : g.M - 1;
+      return (int64_t)nt * C::BNB + r;
     } else if constexpr (MODE == kG1U1) {
-      const int pid = rowinfo[tid];
-      arow = pid < npairs ? pid / g.topk : 0;
+      return (int64_t)expert * 2 * g.N + (r < 128 ? nt * 128 + r : g.N + nt * 128 + (r - 128));
     } else {
-      arow = row0 + tid;
+      return (int64_t)expert * g.N + (int64_t)nt * C::BNB + r;
     }
-    sa_src = g.a_scale + arow * g.ssm;
-  }
-  const uint8_t* b_src[C::kBPerThread];
-  int b_off[C::kBPerThread];
-  const int64_t KBYTES = g.K;
+  };
+
+  // ---- per-lane DMA sources (advance 128 bytes per K step) and wave-uniform LDS offsets
+  const uint8_t* gsrc[C::kQW];
+  int lofs[C::kQW];
 #pragma unroll
-  for (int i = 0; i < C::kBPerThread; ++i) {
-    const int ci = tid + 256 * i;
-    const int r = ci >> 3, ch = ci & 7;
-    int64_t brow;
-    if constexpr (MODE == kDense) {
-      brow = (int64_t)nt * 128 + r;
-    } else if constexpr (MODE == kG1U1) {
-      brow = (int64_t)expert * 2 * g.N + (r < 128 ? nt * 128 + r : g.N + nt * 128 + (r - 128));
+  for (int j = 0; j < C::kQW; ++j) {
+    const int q = w + j * C::NW;
+    const int slot = lane & 7;
+    if (q < C::kAQ) {
+      const int r = q * 8 + (lane >> 3);
+      const int rr = r < C::BM ? r : 0;
+      gsrc[j] = g.a + a_row(rr) * g.K + ((slot ^ ((r >> 1) & 7)) << 4);
+      lofs[j] = C::kAOff + q * 1024;
     } else {
-      brow = (int64_t)expert * g.N + nt * 128 + r;
+      const int r = (q - C::kAQ) * 8 + (lane >> 3);
+      gsrc[j] = g.b + b_row(r) * g.K + ((slot ^ ((r >> 1) & 7)) << 4);
+      lofs[j] = C::kBOff + (q - C::kAQ) * 1024;
     }
-    b_src[i] = g.b + brow * KBYTES + ch * 16;
-    b_off[i] = swz(r, ch);
   }
-  const float* sb_src[C::kParts];
+  const int my_row = wm * C::kWTM + (lane < C::kWTM ? lane : 0);
+  const float* ssrc = g.a_scale + a_row(my_row) * g.ssm;
+  const int sofs = C::kSOff + w * 256;
+
+  // per-wave B scale column block
+  const int part = wn / (C::kWN / C::kParts);
+  const int colofs = (wn % (C::kWN / C::kParts)) * C::kWTNB;  // first output column of this wave in its part
+  const float* sbp;
   if constexpr (MODE == kDense) {
-    sb_src[0] = g.b_scale + (int64_t)nt * KB;
+    sbp = g.b_scale + (int64_t)((nt * C::BNB + wn * C::kWTNB) / 128) * KB;
   } else if constexpr (MODE == kG1U1) {
     const int64_t nb2 = 2 * (g.N / 128);
-    sb_src[0] = g.b_scale + ((int64_t)expert * nb2 + nt) * KB;
-    sb_src[C::kParts - 1] = g.b_scale + ((int64_t)expert * nb2 + g.N / 128 + nt) * KB;
+    sbp = g.b_scale + ((int64_t)expert * nb2 + (part == 0 ? nt : g.N / 128 + nt)) * KB;
   } else {
-    sb_src[0] = g.b_scale + ((int64_t)expert * NT + nt) * KB;
+    sbp = g.b_scale + ((int64_t)expert * (g.N / 128) + (nt * C::BNB + wn * C::kWTNB) / 128) * KB;
   }
 
-  v4f acc[C::kParts][C::kTM][C::kTN];
-#pragma unroll
-  for (int p = 0; p < C::kParts; ++p)
-#pragma unroll
-    for (int tm = 0; tm < C::kTM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < C::kTN; ++tn) acc[p][tm][tn] = v4f{0.f, 0.f, 0.f, 0.f};
+  // this wave's B scales for every K block, fetched before the DMA pipeline starts:
+  // lane L holds blocks L and L + 64 (K <= 16384); read per step with readlane
+  const float sbv0 = lane < KB ? sbp[lane] : 0.0f;
+  const float sbv1 = lane + 64 < KB ? sbp[lane + 64] : 0.0f;
+  vm_wait<0>();  // every ordinary load lands before the first DMA is queued
 
-  u32x4 ra[C::kAPerThread];
-  u32x4 rb[C::kBPerThread];
-  float rsa = 0.0f;
-  const bool a_live = C::kAChunks >= 256 || tid < C::kAChunks;  // only BM = 16 leaves threads idle
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int stage, int kb) {
+    const uint32_t base = lds0 + stage * C::kStage;
+#pragma unroll
+    for (int j = 0; j < C::kQW; ++j)
+      dma16(gsrc[j] + (int64_t)kb * 128, __builtin_amdgcn_readfirstlane(base + lofs[j]));
+    dma4(ssrc + (int64_t)kb * g.sskb, __builtin_amdgcn_readfirstlane(base + sofs));
+  };
 
-  gload_tile<C::kAPerThread, C::kBPerThread>(ra, rb, a_src, b_src, a_live, 0);
-  if (tid < BM) rsa = sa_src[0];
-  lstore_tile<C::kAPerThread, C::kBPerThread>(a_lds[0], b_lds[0], ra, rb, a_off, b_off, a_live);
-  if (tid < BM) sa_lds[0][tid] = rsa;
-  __syncthreads();
+  v4f acc[C::kTM][C::kTN];
+#pragma unroll
+  for (int tm = 0; tm < C::kTM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < C::kTN; ++tn) acc[tm][tn] = v4f{0.f, 0.f, 0.f, 0.f};
+
   const int lr = lane & 15, lg = lane >> 4;
-  for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < KB) {
-      gload_tile<C::kAPerThread, C::kBPerThread>(ra, rb, a_src, b_src, a_live, (int64_t)(kb + 1) * 128);
-      if (tid < BM) rsa = sa_src[(int64_t)(kb + 1) * g.sskb];
-    }
-    float sb[C::kParts];
 #pragma unroll
-    for (int p = 0; p < C::kParts; ++p) sb[p] = sb_src[p][kb];
+  for (int s = 0; s < C::S - 1; ++s)
+    if (s < KB) issue(s, s);
+
+  for (int kb = 0; kb < KB; ++kb) {
+    const int ahead = min(C::S - 2, KB - 1 - kb);
+    vm_wait_stages<C::kLoadsPerStage>(ahead);
+    barrier_only();
+    if (kb + C::S - 1 < KB) issue((kb + C::S - 1) % C::S, kb + C::S - 1);
+
+    const uint8_t* st = lds + (kb % C::S) * C::kStage;
+    const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? sbv0 : sbv1), kb & 63));
     v8i av[C::kTM];
-    v4f sa4[C::kTM];
+    v4f s4[C::kTM];
 #pragma unroll
     for (int tm = 0; tm < C::kTM; ++tm) {
-      av[tm] = lds_frag(a_lds[buf], wm * C::kWTM + tm * 16 + lr, lg);
-      sa4[tm] = *reinterpret_cast<const v4f*>(&sa_lds[buf][wm * C::kWTM + tm * 16 + 4 * lg]);
+      av[tm] = lds_frag(st + C::kAOff, wm * C::kWTM + tm * 16 + lr, lg);
+      s4[tm] = *reinterpret_cast<const v4f*>(st + sofs + (tm * 16 + 4 * lg) * 4) * sb;
     }
+    v8i bv[C::kTN];
 #pragma unroll
-    for (int p = 0; p < C::kParts; ++p) {
-      v8i bv[C::kTN];
+    for (int tn = 0; tn < C::kTN; ++tn) bv[tn] = lds_frag(st + C::kBOff, wn * C::kWTNB + tn * 16 + lr, lg);
+    // rolling window: tile q is issued, tile q-2 is folded
+    constexpr int NQ = C::kTM * C::kTN;
+    v4f tq[3];
 #pragma unroll
-      for (int tn = 0; tn < C::kTN; ++tn) bv[tn] = lds_frag(b_lds[buf], p * 128 + wn * C::kWTN + tn * 16 + lr, lg);
-#pragma unroll
-      for (int tm = 0; tm < C::kTM; ++tm) {
-        const v4f s4 = sa4[tm] * sb[p];
-#pragma unroll
-        for (int tn = 0; tn < C::kTN; ++tn) {
-          const v4f t = mfma16x16x128_fp8(av[tm], bv[tn], v4f{0.f, 0.f, 0.f, 0.f});
-          acc[p][tm][tn] += t * s4;
-        }
+    for (int q = 0; q < NQ + 2; ++q) {
+      if (q < NQ) tq[q % 3] = mfma16x16x128_fp8(av[q % C::kTM], bv[q / C::kTM], v4f{0.f, 0.f, 0.f, 0.f});
+      if (q >= 2) {
+        const int p = q - 2;
+        acc[p % C::kTM][p / C::kTM] += tq[p % 3] * s4[p % C::kTM];
       }
     }
-    if (kb + 1 < KB) {
-      lstore_tile<C::kAPerThread, C::kBPerThread>(a_lds[buf ^ 1], b_lds[buf ^ 1], ra, rb, a_off, b_off, a_live);
-      if (tid < BM) sa_lds[buf ^ 1][tid] = rsa;
-    }
-    __syncthreads();
   }
+  vm_wait<0>();
+  __syncthreads();
 
-  // ---- epilogues
+  // ---- epilogues (LDS is free again)
   if constexpr (MODE == kDense) {
+    // bf16 tile [BM][BNB] in LDS, then 16-byte row stores
+    uint16_t* ob = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
     for (int tm = 0; tm < C::kTM; ++tm)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = row0 + wm * C::kWTM + tm * 16 + 4 * lg + i;
-        if (m < g.M) {
+      for (int tn = 0; tn < C::kTN; ++tn)
 #pragma unroll
-          for (int tn = 0; tn < C::kTN; ++tn) {
-            const int n = nt * 128 + wn * C::kWTN + tn * 16 + lr;
-            g.c[m * g.ldc + n] = (uint16_t)f32_to_bf16(acc[0][tm][tn][i]);
-          }
-        }
-      }
+        for (int i = 0; i < 4; ++i)
+          ob[(wm * C::kWTM + tm * 16 + 4 * lg + i) * C::BNB + wn * C::kWTNB + tn * 16 + lr] =
+              (uint16_t)f32_to_bf16(acc[tm][tn][i]);
+    __syncthreads();
+    constexpr int CPR = C::BNB * 2 / 16;  // 16-byte chunks per row
+    for (int ci = tid; ci < C::BM * CPR; ci += C::kThreads) {
+      const int r = ci / CPR, ch = ci % CPR;
+      const int64_t m = row0 + r;
+      if (m < g.M)
+        *reinterpret_cast<u32x4*>(g.c + m * g.ldc + (int64_t)nt * C::BNB + ch * 8) =
+            *reinterpret_cast<const u32x4*>(ob + r * C::BNB + ch * 8);
+    }
   } else if constexpr (MODE == kDown) {
+    // routing-weighted fp32 tile [BM][BNB] in LDS, then 16-byte stores per pair row
+    float* ob = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int tm = 0; tm < C::kTM; ++tm)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rl = wm * C::kWTM + tm * 16 + 4 * lg + i;
-        const int pid = rowinfo[rl];
-        if (row0 + rl < nvalid && pid < npairs) {
-          const float wgt = g.sorted_w[row0 + rl];
-          float* dst = g.y + (int64_t)pid * g.N + nt * 128 + wn * C::kWTN + lr;
+        const float wgt = rowinfo[rl] < npairs ? g.sorted_w[row0 + rl] : 0.0f;
 #pragma unroll
-          for (int tn = 0; tn < C::kTN; ++tn) dst[tn * 16] = acc[0][tm][tn][i] * wgt;
-        }
+        for (int tn = 0; tn < C::kTN; ++tn) ob[rl * C::BNB + wn * C::kWTNB + tn * 16 + lr] = acc[tm][tn][i] * wgt;
       }
+    __syncthreads();
+    constexpr int CPR = C::BNB * 4 / 16;
+    for (int ci = tid; ci < C::BM * CPR; ci += C::kThreads) {
+      const int r = ci / CPR, ch = ci % CPR;
+      const int pid = rowinfo[r];
+      if (row0 + r < nvalid && pid < npairs)
+        *reinterpret_cast<u32x4*>(g.y + (int64_t)pid * g.N + (int64_t)nt * C::BNB + ch * 4) =
+            *reinterpret_cast<const u32x4*>(ob + r * C::BNB + ch * 4);
+    }
   } else {
-    // h = SiLU(gate) * up, then 1x128 requantisation of each row's 128 columns
-    float rmax[C::kTM][4];
-#pragma unroll
-    for (int tm = 0; tm < C::kTM; ++tm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float mx = 0.0f;
-#pragma unroll
-        for (int tn = 0; tn < C::kTN; ++tn) {
-          const float gt = acc[0][tm][tn][i];
-          const float up = acc[C::kParts - 1][tm][tn][i];
-          const float h = gt / (1.0f + expf(-gt)) * up;
-          acc[0][tm][tn][i] = h;
-          mx = fmaxf(mx, fabsf(h));
-        }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-        rmax[tm][i] = mx;
-      }
-    if (lr == 0) {
+    // gate waves hand their tiles to the up waves with the same lanes; up waves form
+    // h = SiLU(gate) * up, then each row's 128 columns are requantised 1x128.
+    constexpr int HW = C::kWN / 2;  // waves per part along N
+    float* xg = reinterpret_cast<float*>(lds);
+    uint8_t* ob = lds + C::WM * HW * C::kTM * C::kTN * 64 * 16;
+    const int pw = wm * HW + (wn % HW);
+    if (part == 0) {
 #pragma unroll
       for (int tm = 0; tm < C::kTM; ++tm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wn][wm * C::kWTM + tm * 16 + 4 * lg + i] = rmax[tm][i];
+        for (int tn = 0; tn < C::kTN; ++tn)
+          *reinterpret_cast<v4f*>(xg + (((pw * C::kTM + tm) * C::kTN + tn) * 64 + lane) * 4) = acc[tm][tn];
     }
     __syncthreads();
-    uint8_t* obuf = a_lds[0];
-    const int IB = g.N / 128;
+    if (part == 1) {
 #pragma unroll
-    for (int tm = 0; tm < C::kTM; ++tm)
+      for (int tm = 0; tm < C::kTM; ++tm) {
+        float mx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rl = wm * C::kWTM + tm * 16 + 4 * lg + i;
-        float amax = red[0][rl];
+        for (int tn = 0; tn < C::kTN; ++tn) {
+          const v4f gt = *reinterpret_cast<const v4f*>(xg + (((pw * C::kTM + tm) * C::kTN + tn) * 64 + lane) * 4);
 #pragma unroll
-        for (int w2 = 1; w2 < C::kWN; ++w2) amax = fmaxf(amax, red[w2][rl]);
-        const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+          for (int i = 0; i < 4; ++i) {
+            const float h = gt[i] / (1.0f + expf(-gt[i])) * acc[tm][tn][i];
+            acc[tm][tn][i] = h;
+            mx[i] = fmaxf(mx[i], fabsf(h));
+          }
+        }
 #pragma unroll
-        for (int tn = 0; tn < C::kTN; ++tn)
-          obuf[rl * 128 + wn * C::kWTN + tn * 16 + lr] = (uint8_t)f32_to_e4m3(acc[0][tm][tn][i] / s);
-        if (wn == 0 && lr == 0 && rowinfo[rl] < npairs) g.h_scale[(row0 + rl) * IB + nt] = s;
+        for (int i = 0; i < 4; ++i) {
+          float v = mx[i];
+#pragma unroll
+          for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+          if (lr == 0) red[wn % HW][wm * C::kWTM + tm * 16 + 4 * lg + i] = v;
+        }
       }
+    }
     __syncthreads();
-    for (int ci = tid; ci < BM * 8; ci += 256) {
+    if (part == 1) {
+      const int IB = g.N / 128;
+#pragma unroll
+      for (int tm = 0; tm < C::kTM; ++tm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rl = wm * C::kWTM + tm * 16 + 4 * lg + i;
+          float amax = red[0][rl];
+#pragma unroll
+          for (int k2 = 1; k2 < HW; ++k2) amax = fmaxf(amax, red[k2][rl]);
+          const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+#pragma unroll
+          for (int tn = 0; tn < C::kTN; ++tn)
+            ob[rl * 128 + colofs + tn * 16 + lr] = (uint8_t)f32_to_e4m3(acc[tm][tn][i] / s);
+          if (colofs == 0 && lr == 0 && rowinfo[rl] < npairs) g.h_scale[(row0 + rl) * IB + nt] = s;
+        }
+    }
+    __syncthreads();
+    for (int ci = tid; ci < C::BM * 8; ci += C::kThreads) {
       const int rl = ci >> 3, ch = ci & 7;
       if (rowinfo[rl] < npairs)
         *reinterpret_cast<u32x4*>(g.h8 + (row0 + rl) * g.N + nt * 128 + ch * 16) =
-            *reinterpret_cast<const u32x4*>(obuf + rl * 128 + ch * 16);
+            *reinterpret_cast<const u32x4*>(ob + rl * 128 + ch * 16);
     }
   }
 }
@@ -348,20 +409,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<u32x4*>(out + t * ld_out + c8 * 8) = o;
 }
 
-template <int MODE>
-int launch_gemm(const GemmArgs& g, int bm, int64_t mblocks, hipStream_t stream) {
-  const int64_t grid = mblocks * (g.N / 128);
+template <class C, int MODE>
+int launch_cfg(const GemmArgs& g, int64_t mblocks, hipStream_t stream) {
+  if (g.N % C::kOutN != 0) return MOE355_EUNSUPPORTED;
+  const int64_t grid = mblocks * (g.N / C::kOutN);
   if (grid == 0) return MOE355_OK;
   MOE355_CHECK(grid < (1ll << 31), MOE355_EUNSUPPORTED);
-  const dim3 gd((unsigned)grid), bd(256);
+  hipLaunchKernelGGL((bs_gemm_kernel<C, MODE>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, g);
+  return launch_status();
+}
+
+// Tile choice per M tile: small tiles stream weights (decode, small M), 128-row
+// tiles with 8 waves feed the matrix cores (prefill, large M).
+template <int MODE, int BNB = 256>
+int launch_gemm(const GemmArgs& g, int bm, int64_t mblocks, hipStream_t stream) {
   switch (bm) {
-    case 16: hipLaunchKernelGGL((bs_gemm_kernel<16, MODE>), gd, bd, 0, stream, g); break;
-    case 32: hipLaunchKernelGGL((bs_gemm_kernel<32, MODE>), gd, bd, 0, stream, g); break;
-    case 64: hipLaunchKernelGGL((bs_gemm_kernel<64, MODE>), gd, bd, 0, stream, g); break;
-    case 128: hipLaunchKernelGGL((bs_gemm_kernel<128, MODE>), gd, bd, 0, stream, g); break;
+    case 16: return launch_cfg<Cfg<MODE, 16, BNB, 4, 1, 4>, MODE>(g, mblocks, stream);
+    case 32: return launch_cfg<Cfg<MODE, 32, BNB, 4, 1, 4>, MODE>(g, mblocks, stream);
+    case 64: return launch_cfg<Cfg<MODE, 64, BNB, 4, 1, 3>, MODE>(g, mblocks, stream);
+    case 128: return launch_cfg<Cfg<MODE, 128, BNB, 8, 2, 3>, MODE>(g, mblocks, stream);
     default: return MOE355_EUNSUPPORTED;
   }
-  return launch_status();
 }
 
 int check_sorted_capacity(int T, int topk, int E, int block_m, int64_t max_sorted) {
@@ -380,10 +448,11 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
                                    const uint8_t* b8, const float* b_scale, int M, int N, int K, uint16_t* c,
                                    int64_t ldc, hipStream_t stream) {
   MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && ldc >= N, MOE355_EINVAL);
-  MOE355_CHECK(K % 128 == 0 && N % 128 == 0, MOE355_EUNSUPPORTED);
+  MOE355_CHECK(K % 128 == 0 && N % 128 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
   if (M == 0 || N == 0) return MOE355_OK;
   MOE355_CHECK(K > 0 && a8 && a_scale && b8 && b_scale && c && sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
-  MOE355_CHECK(aligned16(a8) && aligned16(b8) && (reinterpret_cast<uintptr_t>(c) & 1u) == 0, MOE355_EMISALIGNED);
+  MOE355_CHECK(aligned16(a8) && aligned16(b8) && aligned16(c) && ldc % 8 == 0, MOE355_EMISALIGNED);
+  MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0, MOE355_EMISALIGNED);
   GemmArgs g{};
   g.a = a8;
   g.a_scale = a_scale;
@@ -397,6 +466,7 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
   g.c = c;
   g.ldc = ldc;
   const int bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+  if (N % 256 != 0) return launch_gemm<kDense, 128>(g, bm, ceil_div64(M, bm), stream);
   return launch_gemm<kDense>(g, bm, ceil_div64(M, bm), stream);
 }
 
@@ -406,7 +476,7 @@ extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, 
                                        int I, int E, int topk, int block_m, int64_t max_sorted, uint8_t* h8,
                                        float* h_scale, hipStream_t stream) {
   MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0, MOE355_EINVAL);
-  MOE355_CHECK(H % 128 == 0 && I % 128 == 0 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
+  MOE355_CHECK(H % 128 == 0 && I % 128 == 0 && H <= 16384 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
   const int cap = check_sorted_capacity(T, topk, E, block_m, max_sorted);
   if (cap != MOE355_OK) return cap;
   if (T == 0) return MOE355_OK;
@@ -414,6 +484,7 @@ extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, 
                MOE355_EINVAL);
   MOE355_CHECK(sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
   MOE355_CHECK(aligned16(a8) && aligned16(w1) && aligned16(h8), MOE355_EMISALIGNED);
+  MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0, MOE355_EMISALIGNED);
   GemmArgs g{};
   g.a = a8;
   g.a_scale = a_scale;
@@ -445,7 +516,7 @@ extern "C" int moe_down_combine(const uint8_t* h8, const float* h_scale, const u
                                 int E, int topk, int block_m, int64_t max_sorted, uint16_t* out, int64_t ld_out,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0 && ld_out >= H, MOE355_EINVAL);
-  MOE355_CHECK(H % 128 == 0 && I % 128 == 0 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
+  MOE355_CHECK(H % 256 == 0 && I % 128 == 0 && I <= 16384 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
   const int cap = check_sorted_capacity(T, topk, E, block_m, max_sorted);
   if (cap != MOE355_OK) return cap;
   if (T == 0) return MOE355_OK;

@@ -86,26 +86,30 @@ def down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sorted_e
     return out
 
 
-def layer_tokens(tokens, a8, a_scale, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights):
-    """Token-major evaluation of the expert part of the layer for selected tokens.
+def layer_tokens(a8, a_scale, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights):
+    """Token-major evaluation of the expert part of the layer for a set of token rows.
 
-    Uses no sort buffer: for each token t and slot j, expert ids[t, j] is
-    applied to row t directly.  Returns (ref float64 [len(tokens), H],
-    h8 uint8 [len, k, I], h_scale float32 [len, k, I/128]).
+    a8 [R, H], a_scale [R, H/128], topk_ids / topk_weights [R, k] are the rows of
+    the tokens to evaluate.  No sort buffer is used: slot j of row i applies
+    expert topk_ids[i, j] to row i.  Each expert is evaluated once on all rows
+    routed to it (rows are independent, so this equals one row at a time).
+    Returns (ref float64 [R, H], h float32 [R, k, I], h8 uint8 [R, k, I],
+    h_scale float32 [R, k, I/128]); ref sums the k weighted outputs in
+    ascending j.
     """
-    tokens = np.asarray(tokens, dtype=np.int64)
+    R, k = topk_ids.shape
     E, H, I = w2.shape
-    k = topk_ids.shape[1]
-    ref = np.zeros((len(tokens), H), dtype=np.float64)
-    h8s = np.zeros((len(tokens), k, I), dtype=np.uint8)
-    hss = np.zeros((len(tokens), k, I // 128), dtype=np.float32)
-    for i, t in enumerate(tokens):
-        for j in range(k):
-            e = int(topk_ids[t, j])
-            h, _ = expert_ffn_h(a8[t:t + 1], a_scale[t:t + 1], w1[e], w1_scale[e])
-            h8, hs = quant.quant_1x128(h)
-            y = gemm.gemm_blockscale(h8, hs, w2[e], w2_scale[e])[0]
-            ref[i] += np.float64(topk_weights[t, j]) * y
-            h8s[i, j] = h8[0]
-            hss[i, j] = hs[0]
-    return ref, h8s, hss
+    y = np.zeros((R, k, H), dtype=np.float64)
+    hh = np.zeros((R, k, I), dtype=np.float32)
+    h8s = np.zeros((R, k, I), dtype=np.uint8)
+    hss = np.zeros((R, k, I // 128), dtype=np.float32)
+    for e in np.unique(topk_ids):
+        ii, jj = np.nonzero(topk_ids == e)
+        h, _ = expert_ffn_h(a8[ii], a_scale[ii], w1[int(e)], w1_scale[int(e)])
+        h8, hs = quant.quant_1x128(h)
+        y[ii, jj] = gemm.gemm_blockscale(h8, hs, w2[int(e)], w2_scale[int(e)])
+        hh[ii, jj], h8s[ii, jj], hss[ii, jj] = h, h8, hs
+    ref = np.zeros((R, H), dtype=np.float64)
+    for j in range(k):
+        ref += np.asarray(topk_weights[:, j], dtype=np.float64)[:, None] * y[:, j]
+    return ref, hh, h8s, hss

@@ -197,8 +197,8 @@ def test_layer_tiny(m, tiny, BM, layout):
     w, ids = oracle_routing(x, cfg)
     assert np.array_equal(layer.topk_ids.cpu().numpy(), ids)
     a8, sa = oracle.quant.quant_1x128(f32_of_bf16(x["hidden"]))
-    ref, _, _ = oracle.moe.layer_tokens(np.arange(cfg.T), a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(),
-                                        x["w2"].numpy(), x["w2_scale"].numpy(), ids, w)
+    ref, _, _, _ = oracle.moe.layer_tokens(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), x["w2"].numpy(),
+                                           x["w2_scale"].numpy(), ids, w)
     assert_rel_max(f32_of_bf16(out), ref, what="tiny layer")
 
 

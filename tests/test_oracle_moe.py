@@ -38,8 +38,12 @@ def test_sorted_path_equals_token_major(rng):
         sid, sw, seid, P = sort.moe_sort(ids, w, w1.shape[0], BM)
         h8, hs, h, valid = moe.g1u1(a8, sa, w1, s1, sid, seid, P, k, BM)
         out = moe.down_combine(h8, hs, w2, s2, sid, sw, seid, P, T, k, BM)
-        ref, h8t, hst = moe.layer_tokens(np.arange(T), a8, sa, w1, s1, w2, s2, ids, w)
+        ref, _, h8t, hst = moe.layer_tokens(a8, sa, w1, s1, w2, s2, ids, w)
         assert np.array_equal(out, ref)
+        # one row at a time gives the same bits
+        for t in range(T):
+            r1, _, _, _ = moe.layer_tokens(a8[t:t + 1], sa[t:t + 1], w1, s1, w2, s2, ids[t:t + 1], w[t:t + 1])
+            assert np.array_equal(r1[0], ref[t])
         for r in np.nonzero(valid)[0]:
             t, j = divmod(int(sid[r]), k)
             assert np.array_equal(h8[r], h8t[t, j]) and np.array_equal(hs[r], hst[t, j])
