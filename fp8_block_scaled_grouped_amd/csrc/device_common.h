@@ -47,7 +47,8 @@ __device__ __forceinline__ float wave_max_f32(float v, int width) {
 }
 
 // D = A(16x128 e4m3) * B(128x16 e4m3) + C.  Lane l holds row/column l%16 and
-// K slots [32*(l/16), 32*(l/16)+32) of A/B; output element (4*(l/16)+i, l%16) in c[i].
+// 32 of the K slots (slots [32*(l/16), 32*(l/16)+32)); A and B must place the
+// same K index in the same slot.  Output element (4*(l/16)+i, l%16) in c[i].
 __device__ __forceinline__ v4f mfma16x16x128_fp8(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }

@@ -10,10 +10,12 @@
 //
 // Data movement: A and B tiles (and the per-row A scales) go HBM -> LDS by
 // LDS-DMA (global_load_lds), S stages deep, with no VGPR staging.  Rows are
-// 128 bytes in LDS with the 16-byte chunk c of row r stored in slot
-// c ^ ((r >> 1) & 7): the 16 lanes that read one chunk of 16 consecutive rows
-// hit 16 different bank groups.  Each wave waits for its own DMAs with
-// s_waitcnt vmcnt and a bare s_barrier publishes the stage.
+// 128 bytes in LDS, 16-byte chunk c of row r in slot c ^ (r & 7); one DMA
+// instruction moves 8 whole rows (full 128-byte lines).  MFMA lane group g
+// (lanes 16g..16g+15) takes K chunks g and g+4 of a 128-wide K block -- any K
+// permutation shared by A and B leaves the product unchanged -- which makes
+// the fragment reads free of LDS bank conflicts.  Each wave waits for its own
+// DMAs with s_waitcnt vmcnt and a bare s_barrier publishes the stage.
 //
 // Modes:
 //   dense  C[M, N] = A[M, K] B[N, K]^T, bf16 out ("General Linear Layer").
@@ -25,6 +27,8 @@
 //   down   grouped GEMM of h with the expert's down weights; each row is
 //          scaled by its routing weight and staged per flat pair; a second
 //          kernel sums each token's pairs in ascending order into bf16.
+#include <type_traits>
+
 #include "device_common.h"
 #include "host_common.h"
 
@@ -84,21 +88,30 @@ struct Cfg {
   static_assert(S >= 2 && S <= 4 && 2 * kLoadsPerStage < 64, "pipeline depth");
 };
 
-__device__ __forceinline__ int swz(int r, int ch) { return r * 128 + ((ch ^ ((r >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// LDS-DMA: every lane moves 16 (or 4) bytes from its global address to
-// LDS[m0 + 16*lane] (or 4*lane).  Issued from asm so that the compiler does not
-// drain the DMA queue before each LDS read; completion is tracked explicitly
-// with vm_wait.  No output registers.
-__device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+// LDS-DMA: every lane moves 16 (or 4) bytes from base + its 32-bit offset to
+// LDS[m0 + 16*lane] (or 4*lane); base is wave-uniform (SGPRs), so advancing a
+// stream costs scalar adds only.  Issued from asm so that the compiler does
+// not drain the DMA queue before each LDS read; completion is tracked
+// explicitly with vm_wait.  No output registers.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0)
+               : "memory");
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(m0)
+               : "memory");
+}
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
 template <int N>
@@ -127,10 +140,14 @@ __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
 }
 
-// MFMA operand of tile row r: K slots [32g, 32g+32) are chunks 2g and 2g+1.
-__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r, int g) {
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + swz(r, 2 * g));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + swz(r, 2 * g + 1));
+__device__ __forceinline__ int swz(int r, int ch) { return r * 128 + ((ch ^ (r & 7)) << 4); }
+
+// MFMA operand for the 16 rows starting at r0: lane l holds row r0 + l%16 with
+// K chunks l/16 (low half) and 4 + l/16 (high half; its slot differs in bit 2).
+__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r0, int lane) {
+  const int off = swz(r0 + (lane & 15), lane >> 4);
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + off);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + (off ^ 64));
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
@@ -144,22 +161,41 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in SGPRs
   const int wm = w / C::kWN, wn = w % C::kWN;
   const int NT = g.N / C::kOutN;
-  const int nt = (int)(blockIdx.x % NT);
-  const int mb = (int)(blockIdx.x / NT);
-  const int64_t row0 = (int64_t)mb * C::BM;
   const int KB = g.K / 128;
   const int npairs = g.T * g.topk;
 
-  int expert = 0, nvalid = 0;
-  if constexpr (MODE != kDense) {
+  // Tiles are (M block, N tile) pairs, N tile fastest, one per workgroup: the N
+  // tiles of an M block share its A rows and run side by side; consecutive M
+  // blocks of one expert share weights.  (Remapping tiles onto XCD-contiguous
+  // ranges measured slower: weight reuse across M blocks matters more.)
+  int64_t total;
+  int nvalid = 0;
+  if constexpr (MODE == kDense) {
+    total = (int64_t)((g.M + C::BM - 1) / C::BM) * NT;
+  } else {
     nvalid = g.num_valid[0];
-    if (row0 >= nvalid) return;  // uniform: no sorted rows in this block
+    total = nvalid > 0 ? (int64_t)(nvalid / C::BM) * NT : 0;
+  }
+  const int64_t tile = blockIdx.x;
+  if (tile >= total) return;  // uniform: blocks past num_valid hold no rows
+  const int nt = (int)(tile % NT);
+  const int mb = (int)(tile / NT);
+  const int64_t row0 = (int64_t)mb * C::BM;
+
+  // valid rows of this block form a prefix (padding sits at the end of an expert's segment)
+  int expert = 0, nrows;
+  if constexpr (MODE != kDense) {
     expert = g.sorted_eids[mb];
     for (int i = tid; i < C::BM; i += C::kThreads) rowinfo[i] = g.sorted_ids[row0 + i];
     __syncthreads();
+    nrows = __syncthreads_count(tid < C::BM && rowinfo[tid < C::BM ? tid : 0] < npairs);
+  } else {
+    nrows = (int)min((int64_t)C::BM, g.M - row0);
   }
+  // MFMA row tiles of this wave holding at least one valid row
+  const int tm_live = __builtin_amdgcn_readfirstlane(min(C::kTM, max(0, (nrows - wm * C::kWTM + 15) / 16)));
 
-  // global row of A-tile row r
+  // A-tile row r -> row of the A operand (relative to g.a)
   auto a_row = [&](int r) -> int64_t {
     if constexpr (MODE == kDense) {
       return row0 + r < g.M ? row0 + r : g.M - 1;
@@ -170,37 +206,48 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
       return row0 + r;
     }
   };
-  // global row of B-tile row r
-  auto b_row = [&](int r) -> int64_t {
-    if constexpr (MODE == kDense) {
-      return (int64_t)nt * C::BNB + r;
-    } else if constexpr (MODE == kG1U1) {
-      return (int64_t)expert * 2 * g.N + (r < 128 ? nt * 128 + r : g.N + nt * 128 + (r - 128));
+  // B-tile row r -> row inside the B base of this workgroup
+  auto b_row = [&](int r) -> int {
+    if constexpr (MODE == kG1U1) {
+      return r < 128 ? nt * 128 + r : g.N + nt * 128 + (r - 128);
     } else {
-      return (int64_t)expert * g.N + (int64_t)nt * C::BNB + r;
+      return nt * C::BNB + r;
     }
   };
+  const uint8_t* a_base = uniform_ptr(g.a);
+  const uint8_t* b_base;
+  if constexpr (MODE == kDense) {
+    b_base = uniform_ptr(g.b);
+  } else if constexpr (MODE == kG1U1) {
+    b_base = uniform_ptr(g.b + (int64_t)expert * 2 * g.N * g.K);
+  } else {
+    b_base = uniform_ptr(g.b + (int64_t)expert * g.N * g.K);
+  }
 
-  // ---- per-lane DMA sources (advance 128 bytes per K step) and wave-uniform LDS offsets
-  const uint8_t* gsrc[C::kQW];
+  // ---- per-lane DMA offsets (fixed) and wave-uniform LDS offsets.
+  // 1 KB block q of a region holds rows 8q .. 8q+7; lane L of its DMA moves the
+  // chunk of row 8q + L/8 that belongs in slot L%8
+  uint32_t voff[C::kQW];
   int lofs[C::kQW];
+  bool is_a[C::kQW];
 #pragma unroll
   for (int j = 0; j < C::kQW; ++j) {
     const int q = w + j * C::NW;
-    const int slot = lane & 7;
-    if (q < C::kAQ) {
-      const int r = q * 8 + (lane >> 3);
-      const int rr = r < C::BM ? r : 0;
-      gsrc[j] = g.a + a_row(rr) * g.K + ((slot ^ ((r >> 1) & 7)) << 4);
+    is_a[j] = q < C::kAQ;
+    const int qq = is_a[j] ? q : q - C::kAQ;
+    const int r = qq * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ (r & 7);
+    if (is_a[j]) {
+      voff[j] = (uint32_t)(a_row(r < C::BM ? r : 0) * g.K + ch * 16);
       lofs[j] = C::kAOff + q * 1024;
     } else {
-      const int r = (q - C::kAQ) * 8 + (lane >> 3);
-      gsrc[j] = g.b + b_row(r) * g.K + ((slot ^ ((r >> 1) & 7)) << 4);
-      lofs[j] = C::kBOff + (q - C::kAQ) * 1024;
+      voff[j] = (uint32_t)((int64_t)b_row(r) * g.K + ch * 16);
+      lofs[j] = C::kBOff + qq * 1024;
     }
   }
   const int my_row = wm * C::kWTM + (lane < C::kWTM ? lane : 0);
-  const float* ssrc = g.a_scale + a_row(my_row) * g.ssm;
+  const uint32_t soff = (uint32_t)(a_row(my_row) * g.ssm * 4);
+  const uint8_t* s_base = uniform_ptr(g.a_scale);
   const int sofs = C::kSOff + w * 256;
 
   // per-wave B scale column block
@@ -225,10 +272,12 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int stage, int kb) {
     const uint32_t base = lds0 + stage * C::kStage;
+    const uint8_t* ak = a_base + (int64_t)kb * 128;
+    const uint8_t* bk = b_base + (int64_t)kb * 128;
 #pragma unroll
     for (int j = 0; j < C::kQW; ++j)
-      dma16(gsrc[j] + (int64_t)kb * 128, __builtin_amdgcn_readfirstlane(base + lofs[j]));
-    dma4(ssrc + (int64_t)kb * g.sskb, __builtin_amdgcn_readfirstlane(base + sofs));
+      dma16(is_a[j] ? ak : bk, voff[j], __builtin_amdgcn_readfirstlane(base + lofs[j]));
+    dma4(s_base + (int64_t)kb * g.sskb * 4, soff, __builtin_amdgcn_readfirstlane(base + sofs));
   };
 
   v4f acc[C::kTM][C::kTN];
@@ -242,35 +291,54 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   for (int s = 0; s < C::S - 1; ++s)
     if (s < KB) issue(s, s);
 
-  for (int kb = 0; kb < KB; ++kb) {
+  // one K step on LDS stage `stage`; only the first TMV row tiles of the wave are computed
+  auto step = [&](const int kb, const int stage, auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
     const int ahead = min(C::S - 2, KB - 1 - kb);
     vm_wait_stages<C::kLoadsPerStage>(ahead);
     barrier_only();
-    if (kb + C::S - 1 < KB) issue((kb + C::S - 1) % C::S, kb + C::S - 1);
-
-    const uint8_t* st = lds + (kb % C::S) * C::kStage;
-    const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? sbv0 : sbv1), kb & 63));
-    v8i av[C::kTM];
-    v4f s4[C::kTM];
+    if (kb + C::S - 1 < KB) issue((stage + C::S - 1) % C::S, kb + C::S - 1);
+    if constexpr (TMV > 0) {
+      const uint8_t* st = lds + stage * C::kStage;
+      const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? sbv0 : sbv1), kb & 63));
+      v8i av[TMV];
+      v4f s4[TMV];
 #pragma unroll
-    for (int tm = 0; tm < C::kTM; ++tm) {
-      av[tm] = lds_frag(st + C::kAOff, wm * C::kWTM + tm * 16 + lr, lg);
-      s4[tm] = *reinterpret_cast<const v4f*>(st + sofs + (tm * 16 + 4 * lg) * 4) * sb;
-    }
-    v8i bv[C::kTN];
+      for (int tm = 0; tm < TMV; ++tm) {
+        av[tm] = lds_frag(st + C::kAOff, wm * C::kWTM + tm * 16, lane);
+        s4[tm] = *reinterpret_cast<const v4f*>(st + sofs + (tm * 16 + 4 * lg) * 4) * sb;
+      }
+      v8i bv[C::kTN];
 #pragma unroll
-    for (int tn = 0; tn < C::kTN; ++tn) bv[tn] = lds_frag(st + C::kBOff, wn * C::kWTNB + tn * 16 + lr, lg);
-    // rolling window: tile q is issued, tile q-2 is folded
-    constexpr int NQ = C::kTM * C::kTN;
-    v4f tq[3];
+      for (int tn = 0; tn < C::kTN; ++tn) bv[tn] = lds_frag(st + C::kBOff, wn * C::kWTNB + tn * 16, lane);
+      // rolling window: tile q is issued, tile q-2 is folded
+      constexpr int NQ = TMV * C::kTN;
+      v4f tq[3];
 #pragma unroll
-    for (int q = 0; q < NQ + 2; ++q) {
-      if (q < NQ) tq[q % 3] = mfma16x16x128_fp8(av[q % C::kTM], bv[q / C::kTM], v4f{0.f, 0.f, 0.f, 0.f});
-      if (q >= 2) {
-        const int p = q - 2;
-        acc[p % C::kTM][p / C::kTM] += tq[p % 3] * s4[p % C::kTM];
+      for (int q = 0; q < NQ + 2; ++q) {
+        if (q < NQ) tq[q % 3] = mfma16x16x128_fp8(av[q % TMV], bv[q / TMV], v4f{0.f, 0.f, 0.f, 0.f});
+        if (q >= 2) {
+          const int p = q - 2;
+          acc[p % TMV][p / TMV] += tq[p % 3] * s4[p % TMV];
+        }
       }
     }
+  };
+  // unrolled by the stage count: every LDS address is base + immediate
+  auto kloop = [&](auto tmv_c) {
+    for (int kb0 = 0; kb0 < KB; kb0 += C::S) {
+#pragma unroll
+      for (int u = 0; u < C::S; ++u)
+        if (kb0 + u < KB) step(kb0 + u, u, tmv_c);
+    }
+  };
+  static_assert(C::kTM <= 4, "row tiles per wave");
+  switch (tm_live) {
+    case 0: kloop(std::integral_constant<int, 0>{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (C::kTM >= 2) kloop(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (C::kTM >= 3) kloop(std::integral_constant<int, 3>{}); break;
+    default: if constexpr (C::kTM >= 4) kloop(std::integral_constant<int, 4>{}); break;
   }
   vm_wait<0>();
   __syncthreads();
@@ -341,7 +409,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
           const v4f gt = *reinterpret_cast<const v4f*>(xg + (((pw * C::kTM + tm) * C::kTN + tn) * 64 + lane) * 4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float h = gt[i] / (1.0f + expf(-gt[i])) * acc[tm][tn][i];
+            const float h = gt[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-gt[i])) * acc[tm][tn][i];
             acc[tm][tn][i] = h;
             mx[i] = fmaxf(mx[i], fabsf(h));
           }
@@ -449,6 +517,7 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
                                    int64_t ldc, hipStream_t stream) {
   MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && ldc >= N, MOE355_EINVAL);
   MOE355_CHECK(K % 128 == 0 && N % 128 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
+  MOE355_CHECK((int64_t)M * K < (1ll << 32) && (int64_t)N * K < (1ll << 32), MOE355_EUNSUPPORTED);
   if (M == 0 || N == 0) return MOE355_OK;
   MOE355_CHECK(K > 0 && a8 && a_scale && b8 && b_scale && c && sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
   MOE355_CHECK(aligned16(a8) && aligned16(b8) && aligned16(c) && ldc % 8 == 0, MOE355_EMISALIGNED);
@@ -477,6 +546,7 @@ extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, 
                                        float* h_scale, hipStream_t stream) {
   MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0, MOE355_EINVAL);
   MOE355_CHECK(H % 128 == 0 && I % 128 == 0 && H <= 16384 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
+  MOE355_CHECK((int64_t)T * H < (1ll << 32) && (int64_t)2 * I * H < (1ll << 32), MOE355_EUNSUPPORTED);
   const int cap = check_sorted_capacity(T, topk, E, block_m, max_sorted);
   if (cap != MOE355_OK) return cap;
   if (T == 0) return MOE355_OK;
@@ -517,6 +587,7 @@ extern "C" int moe_down_combine(const uint8_t* h8, const float* h_scale, const u
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0 && ld_out >= H, MOE355_EINVAL);
   MOE355_CHECK(H % 256 == 0 && I % 128 == 0 && I <= 16384 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
+  MOE355_CHECK(max_sorted * I < (1ll << 32) && (int64_t)H * I < (1ll << 32), MOE355_EUNSUPPORTED);
   const int cap = check_sorted_capacity(T, topk, E, block_m, max_sorted);
   if (cap != MOE355_OK) return cap;
   if (T == 0) return MOE355_OK;

@@ -1,7 +1,8 @@
 // MoE align/sort ("Accelerate DeepSeek-R1 Inference: Integrate AITER into
 // SGLang", section "Complete MoE Implementation" / "MoE Sorting").
 //
-// Three launches on the caller's stream, no host synchronisation:
+// Up to 16384 pairs: one workgroup does everything (see sort_small_kernel).
+// Beyond that, three launches on the caller's stream, no host synchronisation:
 //   count   one workgroup per chunk of 256 flat pairs: per-expert histogram in LDS
 //   scan    one workgroup: per-expert prefix over chunks, padded segment offsets
 //           (exclusive scan over experts), padding sentinels, block -> expert map
@@ -163,6 +164,89 @@ __global__ __launch_bounds__(kChunk) void sort_scatter_kernel(const int32_t* __r
   }
 }
 
+// Small inputs (at most kSmallMaxPairs pairs, e.g. decode): the whole sort in one
+// 1024-thread workgroup -- histogram, padded scan, then the pairs in chunks of
+// 1024 in flat order, each ranked stably (ballots inside a wave, per-wave counts
+// across waves) on top of a running per-expert position.
+constexpr int kSmallMaxPairs = 16384;
+constexpr int kSmallWaves = kScanThreads / kWave;
+
+__global__ __launch_bounds__(kScanThreads) void sort_small_kernel(const int32_t* __restrict__ ids,
+                                                                  const float* __restrict__ weights, int64_t ld,
+                                                                  int T, int k, int E, int BM, int nbits,
+                                                                  int32_t* __restrict__ sorted_ids,
+                                                                  float* __restrict__ sorted_w,
+                                                                  int32_t* __restrict__ sorted_eids,
+                                                                  int32_t* __restrict__ num_valid) {
+  __shared__ int pos[kMaxE];                  // counts, then the next free slot of each expert
+  __shared__ int wcnt[kSmallWaves][kMaxE];    // per-wave counts of one chunk (kept all-zero between uses)
+  __shared__ int wave_tot[kSmallWaves + 1];
+  __shared__ int bad;
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  const int np = T * k;
+  for (int e = tid; e < E; e += kScanThreads) pos[e] = 0;
+  for (int i = tid; i < kSmallWaves * E; i += kScanThreads) wcnt[i / E][i % E] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int p = tid; p < np; p += kScanThreads) {
+    const int e = ids[(int64_t)(p / k) * ld + p % k];
+    if (e >= 0 && e < E)
+      atomicAdd(&pos[e], 1);
+    else
+      atomicAdd(&bad, 1);
+  }
+  __syncthreads();
+  const int c = tid < E ? pos[tid] : 0;
+  const int padded = (c + BM - 1) / BM * BM;
+  int total = 0;
+  const int off = block_exclusive_scan(padded, wave_tot, total);
+  if (tid < E) {
+    const int sentinel = T * k;
+    for (int i = c; i < padded; ++i) {
+      sorted_ids[off + i] = sentinel;
+      sorted_w[off + i] = 0.0f;
+    }
+    for (int b = off / BM; b < (off + padded) / BM; ++b) sorted_eids[b] = tid;
+    pos[tid] = off;
+  }
+  if (tid == 0) num_valid[0] = bad ? -1 : total;
+  __syncthreads();
+  for (int base = 0; base < np; base += kScanThreads) {
+    const int p = base + tid;
+    int e = -1;
+    float wt = 0.0f;
+    if (p < np) {
+      e = ids[(int64_t)(p / k) * ld + p % k];
+      wt = weights[(int64_t)(p / k) * ld + p % k];
+      if (e < 0 || e >= E) e = -1;
+    }
+    uint64_t peers = __ballot(e >= 0);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = e >= 0 && ((e >> bit) & 1);
+      const uint64_t bal = __ballot(on);
+      peers &= on ? bal : ~bal;
+    }
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const int rank_w = __popcll(peers & lt);
+    const bool leader = e >= 0 && rank_w == 0;
+    if (leader) wcnt[w][e] = __popcll(peers);
+    __syncthreads();
+    if (e >= 0) {
+      int before = 0;
+      for (int ww = 0; ww < w; ++ww) before += wcnt[ww][e];
+      const int at = pos[e] + before + rank_w;
+      sorted_ids[at] = p;
+      sorted_w[at] = wt;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&pos[e], __popcll(peers));
+      wcnt[w][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 }  // namespace moe355
 
@@ -193,10 +277,15 @@ extern "C" int moe_sort(const int32_t* topk_ids, const float* topk_weights, int6
                MOE355_EINVAL);
   MOE355_CHECK(workspace_bytes >= need, MOE355_EINVAL);
   MOE355_CHECK((reinterpret_cast<uintptr_t>(workspace) & 3u) == 0, MOE355_EMISALIGNED);
-  const int nc = (int)nchunks_of(T, topk);
-  const SortWs ws = ws_layout(workspace, T, topk, E);
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
+  if ((int64_t)T * topk <= kSmallMaxPairs) {
+    hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(kScanThreads), 0, stream, topk_ids, topk_weights, ld_topk, T,
+                       topk, E, block_m, nbits, sorted_ids, sorted_weights, sorted_expert_ids, num_valid);
+    return launch_status();
+  }
+  const int nc = (int)nchunks_of(T, topk);
+  const SortWs ws = ws_layout(workspace, T, topk, E);
   hipLaunchKernelGGL(sort_count_kernel, dim3(nc), dim3(kChunk), 0, stream, topk_ids, ld_topk, T, topk, E, ws);
   hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, ws, nc, T, topk, E, block_m, sorted_ids,
                      sorted_weights, sorted_expert_ids, num_valid);

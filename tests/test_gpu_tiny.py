@@ -80,7 +80,9 @@ def test_topk_bitexact_tiny(m, tiny, ld_extra):
 
 
 @pytest.mark.parametrize("T,E,G,tg,k,renorm", [(1, 16, 4, 2, 4, True), (33, 64, 8, 3, 6, False), (5, 1024, 64, 8, 32, True),
-                                               (100, 256, 8, 4, 8, True), (7, 24, 3, 2, 5, True)])
+                                               (100, 256, 8, 4, 8, True), (7, 24, 3, 2, 5, True),
+                                               # group shapes off the register path (12 or 24 experts per group)
+                                               (20, 96, 4, 2, 6, True), (9, 48, 4, 3, 5, False), (3, 1000, 8, 2, 9, True)])
 def test_topk_bitexact_shapes(m, T, E, G, tg, k, renorm):
     g = torch.Generator().manual_seed(T * 7 + E)
     logits = torch.randn((T, E), generator=g)
@@ -126,7 +128,8 @@ def test_sort_bitexact_tiny_routing(m, tiny, BM):
     _check_sort(m, ids, w, cfg.E, BM, ld_extra=10)
 
 
-@pytest.mark.parametrize("T,k,E,BM", [(1, 1, 4, 16), (1000, 8, 256, 64), (300, 3, 1024, 16), (4096, 8, 256, 128)])
+@pytest.mark.parametrize("T,k,E,BM", [(1, 1, 4, 16), (1000, 8, 256, 64), (300, 3, 1024, 16), (4096, 8, 256, 128),
+                                      (2048, 8, 256, 32), (2049, 8, 256, 16), (5000, 4, 1000, 64)])
 def test_sort_bitexact_random(m, T, k, E, BM):
     rng = np.random.default_rng(T + E)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
