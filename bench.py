@@ -37,7 +37,47 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after timing, copy BYTES bytes device-to-device 3 times (plain copy kernel whose "
+                         "FETCH_SIZE / WRITE_SIZE calibrate the traffic counters)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ["fp8_block_scaled_grouped_amd/csrc/gemm.hip", "fp8_block_scaled_grouped_amd/csrc/device_common.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it was taken
+    on the current kernel source (else None).  Each counter is scaled by what it read for a
+    plain copy of known size in the same runs."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_hash") != kernel_source_hash() or kernel not in d.get("kernels", {}):
+        return None
+    k = d["kernels"][kernel]
+    cal = d["copy_calibration"]
+    fetch = k["FETCH_SIZE_KiB"] * 1024 * cal["bytes"] / (cal["FETCH_SIZE_KiB"] * 1024)
+    write = k["WRITE_SIZE_KiB"] * 1024 * cal["bytes"] / (cal["WRITE_SIZE_KiB"] * 1024)
+    return fetch + write
+
+
+def copy_calibration(nbytes):
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def routing_stats(ids, E, block_m, hot=None):
@@ -178,7 +218,7 @@ def bench_moe(a):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = "moe_fp8_blockscale_g1u1"
     roof["kernel_ms"] = g1u1_ms
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(a.workload, "g1u1")
 
     res = {
         "metric": "FP8 blockscale MoE layer tokens/s", "value": T / (ms * 1e-3), "unit": "tokens/s",
@@ -238,7 +278,8 @@ def bench_dense(a):
     else:
         roof = {"bound": "mfma", "achieved": flops / (gms * 1e-3) / 1e12, "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
-    roof.update(frac=roof["achieved"] / roof["peak"], kernel="gemm_fp8_blockscale", kernel_ms=gms, traffic=None)
+    roof.update(frac=roof["achieved"] / roof["peak"], kernel="gemm_fp8_blockscale", kernel_ms=gms,
+                traffic=measured_traffic("dense_%d_%d" % (M, N), "dense"))
     return {"metric": "FP8 blockscale dense GEMM TFLOP/s", "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
             "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic",
@@ -254,6 +295,8 @@ def main():
               "run without --gpus or with --gpus 1", file=sys.stderr)
         sys.exit(2)
     res = bench_dense(a) if a.workload == "dense" else bench_moe(a)
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
     print(json.dumps(res), flush=True)
 
 
