@@ -27,6 +27,7 @@
 //   down   grouped GEMM of h with the expert's down weights; each row is
 //          scaled by its routing weight and staged per flat pair; a second
 //          kernel sums each token's pairs in ascending order into bf16.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -56,6 +57,8 @@ struct GemmArgs {
   uint8_t* h8;             // g1u1 out [max_sorted, N]
   float* h_scale;          // g1u1 out [max_sorted, N/128]
   float* y;                // down staging [T*topk, N] fp32
+  int splits, kbs;         // dense split-K: K blocks [ks*kbs, ks*kbs+kbs) per split ks
+  float* part;             // dense split-K partial sums [splits, M, N] fp32
 };
 
 // Tile configuration.  BNB = B rows staged per workgroup (g1u1: 128 gate + 128 up).
@@ -161,13 +164,14 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in SGPRs
   const int wm = w / C::kWN, wn = w % C::kWN;
   const int NT = g.N / C::kOutN;
-  const int KB = g.K / 128;
+  const int KBtot = g.K / 128;  // K blocks of the whole problem (row stride of the B scales)
   const int npairs = g.T * g.topk;
 
   // Tiles are (M block, N tile) pairs, N tile fastest, one per workgroup: the N
   // tiles of an M block share its A rows and run side by side; consecutive M
   // blocks of one expert share weights.  (Remapping tiles onto XCD-contiguous
   // ranges measured slower: weight reuse across M blocks matters more.)
+  // Dense split-K: tile index = split * (M blocks * N tiles) + M block * N tiles + N tile.
   int64_t total;
   int nvalid = 0;
   if constexpr (MODE == kDense) {
@@ -176,8 +180,16 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     nvalid = g.num_valid[0];
     total = nvalid > 0 ? (int64_t)(nvalid / C::BM) * NT : 0;
   }
-  const int64_t tile = blockIdx.x;
+  int64_t tile = blockIdx.x;
+  int ks = 0;
+  if constexpr (MODE == kDense) {
+    ks = (int)(tile / total);
+    tile -= (int64_t)ks * total;
+    if (ks >= g.splits) return;
+  }
   if (tile >= total) return;  // uniform: blocks past num_valid hold no rows
+  const int kbase = ks * g.kbs;                        // first K block of this split
+  const int KB = min(g.kbs, KBtot - kbase);            // K blocks this workgroup walks
   const int nt = (int)(tile % NT);
   const int mb = (int)(tile / NT);
   const int64_t row0 = (int64_t)mb * C::BM;
@@ -255,12 +267,12 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   const int colofs = (wn % (C::kWN / C::kParts)) * C::kWTNB;  // first output column of this wave in its part
   const float* sbp;
   if constexpr (MODE == kDense) {
-    sbp = g.b_scale + (int64_t)((nt * C::BNB + wn * C::kWTNB) / 128) * KB;
+    sbp = g.b_scale + (int64_t)((nt * C::BNB + wn * C::kWTNB) / 128) * KBtot + kbase;
   } else if constexpr (MODE == kG1U1) {
     const int64_t nb2 = 2 * (g.N / 128);
-    sbp = g.b_scale + ((int64_t)expert * nb2 + (part == 0 ? nt : g.N / 128 + nt)) * KB;
+    sbp = g.b_scale + ((int64_t)expert * nb2 + (part == 0 ? nt : g.N / 128 + nt)) * KBtot;
   } else {
-    sbp = g.b_scale + ((int64_t)expert * (g.N / 128) + (nt * C::BNB + wn * C::kWTNB) / 128) * KB;
+    sbp = g.b_scale + ((int64_t)expert * (g.N / 128) + (nt * C::BNB + wn * C::kWTNB) / 128) * KBtot;
   }
 
   // this wave's B scales for every K block, fetched before the DMA pipeline starts:
@@ -272,12 +284,13 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int stage, int kb) {
     const uint32_t base = lds0 + stage * C::kStage;
-    const uint8_t* ak = a_base + (int64_t)kb * 128;
-    const uint8_t* bk = b_base + (int64_t)kb * 128;
+    const int64_t kg = kbase + kb;  // K block in the whole problem
+    const uint8_t* ak = a_base + kg * 128;
+    const uint8_t* bk = b_base + kg * 128;
 #pragma unroll
     for (int j = 0; j < C::kQW; ++j)
       dma16(is_a[j] ? ak : bk, voff[j], __builtin_amdgcn_readfirstlane(base + lofs[j]));
-    dma4(s_base + (int64_t)kb * g.sskb * 4, soff, __builtin_amdgcn_readfirstlane(base + sofs));
+    dma4(s_base + kg * g.sskb * 4, soff, __builtin_amdgcn_readfirstlane(base + sofs));
   };
 
   v4f acc[C::kTM][C::kTN];
@@ -333,6 +346,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     }
   };
   static_assert(C::kTM <= 4, "row tiles per wave");
+  static_assert(C::BM * C::BNB * 4 <= C::kLds, "fp32 output tile fits the pipeline LDS");
   switch (tm_live) {
     case 0: kloop(std::integral_constant<int, 0>{}); break;
     case 1: kloop(std::integral_constant<int, 1>{}); break;
@@ -344,7 +358,27 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   __syncthreads();
 
   // ---- epilogues (LDS is free again)
-  if constexpr (MODE == kDense) {
+  if (MODE == kDense && g.splits > 1) {
+    // split-K partial: fp32 tile [BM][BNB] in LDS, then 16-byte stores into part[ks]
+    float* ob = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int tm = 0; tm < C::kTM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < C::kTN; ++tn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ob[(wm * C::kWTM + tm * 16 + 4 * lg + i) * C::BNB + wn * C::kWTNB + tn * 16 + lr] = acc[tm][tn][i];
+    __syncthreads();
+    constexpr int CPR = C::BNB * 4 / 16;
+    float* dst = g.part + (int64_t)ks * g.M * g.N;
+    for (int ci = tid; ci < C::BM * CPR; ci += C::kThreads) {
+      const int r = ci / CPR, ch = ci % CPR;
+      const int64_t m = row0 + r;
+      if (m < g.M)
+        *reinterpret_cast<u32x4*>(dst + m * g.N + (int64_t)nt * C::BNB + ch * 4) =
+            *reinterpret_cast<const u32x4*>(ob + r * C::BNB + ch * 4);
+    }
+  } else if constexpr (MODE == kDense) {
     // bf16 tile [BM][BNB] in LDS, then 16-byte row stores
     uint16_t* ob = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
@@ -477,10 +511,50 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<u32x4*>(out + t * ld_out + c8 * 8) = o;
 }
 
+// c[m, n] = bf16 of the fp32 sum of part[split, m, n] over the splits, in a fixed
+// order: wave w sums splits w, w+4, w+8, ... in ascending order, then the four
+// wave sums are added in wave order.  One workgroup covers 256 columns of one
+// row; every lane keeps up to 8 loads in flight.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                                            uint16_t* __restrict__ c, int64_t ldc) {
+  __shared__ float sh[4][256];
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int m = blockIdx.y;
+  const int col = blockIdx.x * 256 + lane * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (col < N) {
+    const float* p = part + (int64_t)m * N + col;
+    const int64_t sstride = (int64_t)M * N;
+    for (int k0 = w; k0 < splits; k0 += 32) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + 4 * u < splits) v[u] = *reinterpret_cast<const float4*>(p + (k0 + 4 * u) * sstride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + 4 * u < splits) {
+          acc.x += v[u].x;
+          acc.y += v[u].y;
+          acc.z += v[u].z;
+          acc.w += v[u].w;
+        }
+    }
+  }
+  *reinterpret_cast<float4*>(&sh[w][lane * 4]) = acc;
+  __syncthreads();
+  if (w == 0 && col < N) {
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = ((sh[0][lane * 4 + i] + sh[1][lane * 4 + i]) + sh[2][lane * 4 + i]) + sh[3][lane * 4 + i];
+    const uint2 r{f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16), f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16)};
+    *reinterpret_cast<uint2*>(c + (int64_t)m * ldc + col) = r;
+  }
+}
+
 template <class C, int MODE>
 int launch_cfg(const GemmArgs& g, int64_t mblocks, hipStream_t stream) {
   if (g.N % C::kOutN != 0) return MOE355_EUNSUPPORTED;
-  const int64_t grid = mblocks * (g.N / C::kOutN);
+  const int64_t grid = mblocks * (g.N / C::kOutN) * (MODE == kDense ? g.splits : 1);
   if (grid == 0) return MOE355_OK;
   MOE355_CHECK(grid < (1ll << 31), MOE355_EUNSUPPORTED);
   hipLaunchKernelGGL((bs_gemm_kernel<C, MODE>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, g);
@@ -500,6 +574,41 @@ int launch_gemm(const GemmArgs& g, int bm, int64_t mblocks, hipStream_t stream) 
   }
 }
 
+// Dense tiling: M tile, B rows per workgroup and K splits.  When M <= 64 leaves
+// fewer output tiles than compute units, K is split so that the grid comes close
+// to one workgroup per compute unit (kSplitTargetWG) without going over: short K
+// loops per workgroup lose more to pipeline fill and epilogue than a second
+// round of workgroups gains.  The fp32 partials (written once, read once) are
+// capped at 1/kSplitBytesDiv of the weight bytes: splits * M * N * 4 <= N * K /
+// kSplitBytesDiv.  Each split walks at least two K blocks.
+constexpr int64_t kSplitTargetWG = 256;
+constexpr int64_t kSplitBytesDiv = 4;
+constexpr int kNarrowMaxN = 4096;  // M <= 64: 128-column tiles up to this N, 256 above
+
+struct DensePlan {
+  int bm, bnb, splits, kbs;
+};
+
+DensePlan dense_plan(int M, int N, int K) {
+  DensePlan p;
+  p.bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+  p.bnb = (N % 256 != 0 || (M <= 64 && N <= kNarrowMaxN)) ? 128 : 256;
+  const int KB = K / 128;
+  const int64_t base = ceil_div64(M, p.bm) * (N / p.bnb);
+  int splits = 1;
+  if (M <= 64 && 2 * base <= kSplitTargetWG && KB >= 4) {
+    const int64_t by_bytes = std::max<int64_t>(1, K / (kSplitBytesDiv * 4 * M));
+    splits = (int)std::min<int64_t>({(int64_t)KB / 2, kSplitTargetWG / base, by_bytes});
+  }
+  p.kbs = (int)ceil_div64(KB, splits);
+  p.splits = (int)ceil_div64(KB, p.kbs);
+  return p;
+}
+
+size_t dense_workspace_bytes(const DensePlan& p, int M, int N) {
+  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) + 256 : 0;
+}
+
 int check_sorted_capacity(int T, int topk, int E, int block_m, int64_t max_sorted) {
   int64_t need = 0;
   const int st = moe_sort_sizes(T, topk, E, block_m, &need, nullptr, nullptr);
@@ -512,9 +621,16 @@ int check_sorted_capacity(int T, int topk, int E, int block_m, int64_t max_sorte
 
 using namespace moe355;
 
+extern "C" int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes) {
+  MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && bytes, MOE355_EINVAL);
+  MOE355_CHECK(K % 128 == 0 && N % 128 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
+  *bytes = (M == 0 || N == 0 || K == 0) ? 0 : dense_workspace_bytes(dense_plan(M, N, K), M, N);
+  return MOE355_OK;
+}
+
 extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb,
                                    const uint8_t* b8, const float* b_scale, int M, int N, int K, uint16_t* c,
-                                   int64_t ldc, hipStream_t stream) {
+                                   int64_t ldc, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && ldc >= N, MOE355_EINVAL);
   MOE355_CHECK(K % 128 == 0 && N % 128 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
   MOE355_CHECK((int64_t)M * K < (1ll << 32) && (int64_t)N * K < (1ll << 32), MOE355_EUNSUPPORTED);
@@ -522,6 +638,15 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
   MOE355_CHECK(K > 0 && a8 && a_scale && b8 && b_scale && c && sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
   MOE355_CHECK(aligned16(a8) && aligned16(b8) && aligned16(c) && ldc % 8 == 0, MOE355_EMISALIGNED);
   MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0, MOE355_EMISALIGNED);
+  DensePlan plan = dense_plan(M, N, K);
+  const size_t need = dense_workspace_bytes(plan, M, N);
+  if (need == 0 || workspace == nullptr || workspace_bytes < need) {
+    // without (enough) workspace: one workgroup per output tile walks all of K
+    plan.splits = 1;
+    plan.kbs = K / 128;
+  } else {
+    MOE355_CHECK(aligned16(workspace), MOE355_EMISALIGNED);
+  }
   GemmArgs g{};
   g.a = a8;
   g.a_scale = a_scale;
@@ -534,9 +659,16 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
   g.K = K;
   g.c = c;
   g.ldc = ldc;
-  const int bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
-  if (N % 256 != 0) return launch_gemm<kDense, 128>(g, bm, ceil_div64(M, bm), stream);
-  return launch_gemm<kDense>(g, bm, ceil_div64(M, bm), stream);
+  g.splits = plan.splits;
+  g.kbs = plan.kbs;
+  g.part = static_cast<float*>(workspace);
+  const int64_t mblocks = ceil_div64(M, plan.bm);
+  const int st = plan.bnb == 128 ? launch_gemm<kDense, 128>(g, plan.bm, mblocks, stream)
+                                 : launch_gemm<kDense, 256>(g, plan.bm, mblocks, stream);
+  if (st != MOE355_OK || plan.splits == 1) return st;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)ceil_div64(N, 256), (unsigned)M), dim3(256), 0, stream,
+                     g.part, plan.splits, M, N, c, ldc);
+  return launch_status();
 }
 
 extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb,
@@ -571,6 +703,8 @@ extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, 
   g.topk = topk;
   g.h8 = h8;
   g.h_scale = h_scale;
+  g.splits = 1;
+  g.kbs = H / 128;
   return launch_gemm<kG1U1>(g, block_m, max_sorted / block_m, stream);
 }
 
@@ -615,6 +749,8 @@ extern "C" int moe_down_combine(const uint8_t* h8, const float* h_scale, const u
   g.T = T;
   g.topk = topk;
   g.y = static_cast<float*>(workspace);
+  g.splits = 1;
+  g.kbs = I / 128;
   int st = launch_gemm<kDown>(g, block_m, max_sorted / block_m, stream);
   if (st != MOE355_OK) return st;
   const int64_t threads = (int64_t)T * (H / 8);

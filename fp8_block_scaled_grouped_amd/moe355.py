@@ -30,7 +30,8 @@ _SIGNATURES = {
     "moe_down_combine_workspace": ([_i32, _i32, _i32, _PSZ], _i32),
     "moe_down_combine": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _vp,
                           _i64, _vp, _sz, _vp], _i32),
-    "gemm_fp8_blockscale": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _vp], _i32),
+    "gemm_fp8_blockscale_workspace": ([_i32, _i32, _i32, _PSZ], _i32),
+    "gemm_fp8_blockscale": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _vp, _sz, _vp], _i32),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -210,17 +211,31 @@ def moe_down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sort
 
 
 # ----------------------------------------------------------------- dense
-def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row"):
-    """a8 e4m3 [M, K] (1x128 scales), b8 e4m3 [N, K] (128x128 scales) -> bf16 [M, N]."""
+def gemm_fp8_blockscale_workspace(M, N, K):
+    b = ctypes.c_size_t()
+    _check(lib().gemm_fp8_blockscale_workspace(M, N, K, ctypes.byref(b)))
+    return b.value
+
+
+def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row", workspace=None):
+    """a8 e4m3 [M, K] (1x128 scales), b8 e4m3 [N, K] (128x128 scales) -> bf16 [M, N].
+
+    workspace: None allocates what gemm_fp8_blockscale_workspace asks for; False runs
+    without workspace (no split-K); or a device uint8 tensor.
+    """
     _dev(a8, torch.uint8, "a8")
     _dev(b8, torch.uint8, "b8")
     M, K = a8.shape
     N = b8.shape[0]
     if c is None:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=a8.device)
+    if workspace is None:
+        n = gemm_fp8_blockscale_workspace(M, N, K)
+        workspace = torch.empty(n, dtype=torch.uint8, device=a8.device) if n else False
+    ws_ptr, ws_n = (None, 0) if workspace is False else (_ptr(workspace), workspace.numel())
     ssm, sskb = _scale_strides(a_scale, M, K, scale_layout)
     _check(lib().gemm_fp8_blockscale(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(b8), _ptr(b_scale), M, N, K, _ptr(c),
-                                     _rows(c, "c"), _stream()))
+                                     _rows(c, "c"), ws_ptr, ws_n, _stream()))
     return c
 
 

@@ -171,19 +171,28 @@ int moe_down_combine(const uint8_t* h8, const float* h_scale,
                      uint16_t* out, int64_t ld_out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* Host-only workspace query for gemm_fp8_blockscale (no GPU access): the bytes of
+ * fp32 partial sums its split-K path uses for this shape (0 when it does not split). */
+int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes);
+
 /*
  * Dense FP8 block-scale GEMM ("General Linear Layer": Y = (XQ, 1x128 scales)
  * times (WQ, 128x128 scales)^T with WQ stored [N, K]):
  *   c[m,n] = bf16( sum_kb a_scale(m,kb) * b_scale[n/128, kb] * sum_{k in kb} a8[m,k] * b8[n,k] )
  * a8       e4m3 [M, K] (row stride K); a_scale(m,kb) = a_scale[m*sstride_m + kb*sstride_kb].
  * b8       e4m3 [N, K] (row stride K); b_scale fp32 [N/128, K/128].
- * c        bf16 bits [M, N] out, row stride ldc >= N.
- * K % 128 == 0, N % 128 == 0; a8, b8 16-byte aligned.
+ * c        bf16 bits [M, N] out, row stride ldc >= N (16-byte aligned rows).
+ * workspace device memory of gemm_fp8_blockscale_workspace() bytes, or NULL / 0: small M
+ *          then splits K over more workgroups, keeps fp32 partial sums there and adds them
+ *          in a fixed order (deterministic); without it one workgroup per output
+ *          tile walks all of K.  Contents need no initialisation.
+ * K % 128 == 0, N % 128 == 0, K <= 16384; a8, b8 16-byte aligned.
  */
 int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale,
                         int64_t sstride_m, int64_t sstride_kb,
                         const uint8_t* b8, const float* b_scale,
                         int M, int N, int K, uint16_t* c, int64_t ldc,
+                        void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
 #ifdef __cplusplus

@@ -27,7 +27,7 @@ def lib():
 def test_header_declares_the_six_calls():
     d = _declared()
     for name in ["grouped_topk", "moe_sort", "fp8_quant_1x128", "moe_fp8_blockscale_g1u1", "moe_down_combine",
-                 "gemm_fp8_blockscale", "moe_sort_sizes", "moe_down_combine_workspace", "moe355_strerror"]:
+                 "gemm_fp8_blockscale", "gemm_fp8_blockscale_workspace", "moe_sort_sizes", "moe_down_combine_workspace", "moe355_strerror"]:
         assert name in d, name
 
 
@@ -72,8 +72,8 @@ def test_invalid_arguments_return_codes(lib):
     assert L.fp8_quant_1x128(_p(8), 256, 4, 256, _p(), 256, _p(), 2, 1, None) == -3
     assert L.fp8_quant_1x128(_p(), 128, 4, 256, _p(), 256, _p(), 2, 1, None) == -1
     # dense GEMM: N % 128 -> EUNSUPPORTED; ldc < N -> EINVAL
-    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 100, 256, _p(), 100, None) == -2
-    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 64, None) == -1
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 100, 256, _p(), 100, None, 0, None) == -2
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 64, None, 0, None) == -1
     # sort: workspace too small -> EINVAL; bad block_m -> EUNSUPPORTED
     assert L.moe_sort(_p(), _p(), 4, 16, 4, 16, 16, _p(), _p(), _p(), _p(), _p(), 1, None) == -1
     assert L.moe_sort(_p(), _p(), 4, 16, 4, 16, 24, _p(), _p(), _p(), _p(), _p(), 1 << 20, None) == -2
@@ -85,3 +85,17 @@ def test_invalid_arguments_return_codes(lib):
     # down: workspace too small
     assert L.moe_down_combine(_p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16, 304, _p(),
                               256, _p(), 8, None) == -1
+
+
+def test_dense_workspace_query(lib):
+    from fp8_block_scaled_grouped_amd import moe355
+    # small M splits K (needs fp32 partials), large M does not
+    for M, N in [(1, 2048), (1, 18432), (64, 2048), (16, 7168)]:
+        n = moe355.gemm_fp8_blockscale_workspace(M, N, 7168)
+        assert n >= 2 * M * N * 4, (M, N, n)
+        assert n <= M * N * 4 * 56 + 256
+    assert moe355.gemm_fp8_blockscale_workspace(4096, 18432, 7168) == 0
+    assert moe355.gemm_fp8_blockscale_workspace(0, 2048, 7168) == 0
+    assert moe355.gemm_fp8_blockscale_workspace(1, 2048, 256) == 0  # two K blocks: nothing to split
+    with pytest.raises(moe355.Moe355Error):
+        moe355.gemm_fp8_blockscale_workspace(1, 100, 256)

@@ -215,15 +215,35 @@ def test_layer_tiny_deterministic(m, tiny):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 384, 512), (37, 384, 512), (128, 256, 1024), (200, 128, 256), (16, 2048, 7168)])
+# (5, 1024, 4096): 16 splits of 2 K blocks; (33, 256, 1664): 3 splits of 5, 5, 3 K blocks
+@pytest.mark.parametrize("M,N,K", [(1, 384, 512), (37, 384, 512), (128, 256, 1024), (200, 128, 256), (16, 2048, 7168),
+                                   (5, 1024, 4096), (33, 256, 1664)])
 @pytest.mark.parametrize("layout", ["row", "kblock"])
-def test_dense_small(m, M, N, K, layout):
+@pytest.mark.parametrize("split", [True, False], ids=["ws", "nows"])
+def test_dense_small(m, M, N, K, layout, split):
     from fp8_block_scaled_grouped_amd import inputs
     d = inputs.make_dense_inputs(M, N, K, "cpu", seed=M + N)
     a8, sa = oracle.quant.quant_1x128(f32_of_bf16(d["a"]))
     sa_dev = torch.from_numpy(sa if layout == "row" else np.ascontiguousarray(sa.T)).to(DEV)
+    ws = None
+    if split:
+        # garbage in the workspace must not matter
+        nws = m.gemm_fp8_blockscale_workspace(M, N, K)
+        ws = torch.full((max(nws, 16),), 0x7F, dtype=torch.uint8, device=DEV)
     c = m.gemm_fp8_blockscale(torch.from_numpy(a8).to(DEV), sa_dev, d["b"].to(DEV), d["b_scale"].to(DEV),
-                              scale_layout=layout)
+                              scale_layout=layout, workspace=ws if split else False)
     torch.cuda.synchronize()
     ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
     assert_rel_max(f32_of_bf16(c), ref, what="dense %dx%dx%d" % (M, N, K))
+
+
+def test_dense_split_deterministic(m):
+    from fp8_block_scaled_grouped_amd import inputs
+    M, N, K = 3, 2048, 7168
+    assert m.gemm_fp8_blockscale_workspace(M, N, K) > 0
+    d = inputs.make_dense_inputs(M, N, K, DEV, seed=5)
+    a8, sa = m.fp8_quant_1x128(d["a"])
+    c1 = m.gemm_fp8_blockscale(a8, sa, d["b"], d["b_scale"]).clone()
+    c2 = m.gemm_fp8_blockscale(a8, sa, d["b"], d["b_scale"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
