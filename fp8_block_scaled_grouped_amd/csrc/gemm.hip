@@ -83,6 +83,9 @@ struct Cfg {
   static constexpr int kSOff = kBOff + kBQ * 1024;
   static constexpr int kStage = kSOff + NW * 256;     // 64 fp32 A scales per wave
   static constexpr int kLds = S * kStage;
+  // g1u1 epilogue: threads per output row (each takes 128 / kQPR columns)
+  static constexpr int kQPR = kThreads / BM >= 8 ? 8 : 4;
+  static constexpr int kRed = kQPR > kWN ? kQPR : kWN;
   static_assert(kWTM % 16 == 0 && kWTNB % 16 == 0, "wave tile must be whole MFMA tiles");
   static_assert(kWTNB <= 128 && 128 % kWTNB == 0, "a wave's columns lie in one 128-column scale block");
   static_assert(kWTM <= 64, "one A-scale DMA per wave covers 64 rows");
@@ -158,7 +161,7 @@ template <class C, int MODE>
 __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLds];
   __shared__ int rowinfo[C::BM];
-  __shared__ float red[C::kWN][C::BM];
+  __shared__ float red[C::kRed][C::BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in SGPRs
@@ -196,8 +199,27 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
 
   // valid rows of this block form a prefix (padding sits at the end of an expert's segment)
   int expert = 0, nrows;
+  if constexpr (MODE != kDense) expert = g.sorted_eids[mb];
+
+  // per-wave B scale column block
+  const int part = wn / (C::kWN / C::kParts);
+  const int colofs = (wn % (C::kWN / C::kParts)) * C::kWTNB;  // first output column of this wave in its part
+  const float* sbp;
+  if constexpr (MODE == kDense) {
+    sbp = g.b_scale + (int64_t)((nt * C::BNB + wn * C::kWTNB) / 128) * KBtot + kbase;
+  } else if constexpr (MODE == kG1U1) {
+    const int64_t nb2 = 2 * (g.N / 128);
+    sbp = g.b_scale + ((int64_t)expert * nb2 + (part == 0 ? nt : g.N / 128 + nt)) * KBtot;
+  } else {
+    sbp = g.b_scale + ((int64_t)expert * (g.N / 128) + (nt * C::BNB + wn * C::kWTNB) / 128) * KBtot;
+  }
+
+  // this wave's B scales for every K block, fetched before the DMA pipeline starts:
+  // lane L holds blocks L and L + 64 (K <= 16384); read per step with readlane
+  const float sbv0 = lane < KB ? sbp[lane] : 0.0f;
+  const float sbv1 = lane + 64 < KB ? sbp[lane + 64] : 0.0f;
+
   if constexpr (MODE != kDense) {
-    expert = g.sorted_eids[mb];
     for (int i = tid; i < C::BM; i += C::kThreads) rowinfo[i] = g.sorted_ids[row0 + i];
     __syncthreads();
     nrows = __syncthreads_count(tid < C::BM && rowinfo[tid < C::BM ? tid : 0] < npairs);
@@ -239,58 +261,43 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   // ---- per-lane DMA offsets (fixed) and wave-uniform LDS offsets.
   // 1 KB block q of a region holds rows 8q .. 8q+7; lane L of its DMA moves the
   // chunk of row 8q + L/8 that belongs in slot L%8
+  // (A blocks come first and B blocks follow, so block q sits at q * 1 KB of a stage)
+  static_assert(C::kAOff == 0 && C::kBOff == C::kAQ * 1024, "stage layout");
   uint32_t voff[C::kQW];
-  int lofs[C::kQW];
-  bool is_a[C::kQW];
 #pragma unroll
   for (int j = 0; j < C::kQW; ++j) {
     const int q = w + j * C::NW;
-    is_a[j] = q < C::kAQ;
-    const int qq = is_a[j] ? q : q - C::kAQ;
+    const bool is_a = q < C::kAQ;
+    const int qq = is_a ? q : q - C::kAQ;
     const int r = qq * 8 + (lane >> 3);
     const int ch = (lane & 7) ^ (r & 7);
-    if (is_a[j]) {
-      voff[j] = (uint32_t)(a_row(r < C::BM ? r : 0) * g.K + ch * 16);
-      lofs[j] = C::kAOff + q * 1024;
-    } else {
-      voff[j] = (uint32_t)((int64_t)b_row(r) * g.K + ch * 16);
-      lofs[j] = C::kBOff + qq * 1024;
-    }
+    voff[j] = is_a ? (uint32_t)(a_row(r < C::BM ? r : 0) * g.K + ch * 16)
+                   : (uint32_t)((int64_t)b_row(r) * g.K + ch * 16);
   }
   const int my_row = wm * C::kWTM + (lane < C::kWTM ? lane : 0);
   const uint32_t soff = (uint32_t)(a_row(my_row) * g.ssm * 4);
   const uint8_t* s_base = uniform_ptr(g.a_scale);
   const int sofs = C::kSOff + w * 256;
 
-  // per-wave B scale column block
-  const int part = wn / (C::kWN / C::kParts);
-  const int colofs = (wn % (C::kWN / C::kParts)) * C::kWTNB;  // first output column of this wave in its part
-  const float* sbp;
-  if constexpr (MODE == kDense) {
-    sbp = g.b_scale + (int64_t)((nt * C::BNB + wn * C::kWTNB) / 128) * KBtot + kbase;
-  } else if constexpr (MODE == kG1U1) {
-    const int64_t nb2 = 2 * (g.N / 128);
-    sbp = g.b_scale + ((int64_t)expert * nb2 + (part == 0 ? nt : g.N / 128 + nt)) * KBtot;
-  } else {
-    sbp = g.b_scale + ((int64_t)expert * (g.N / 128) + (nt * C::BNB + wn * C::kWTNB) / 128) * KBtot;
-  }
-
-  // this wave's B scales for every K block, fetched before the DMA pipeline starts:
-  // lane L holds blocks L and L + 64 (K <= 16384); read per step with readlane
-  const float sbv0 = lane < KB ? sbp[lane] : 0.0f;
-  const float sbv1 = lane + 64 < KB ? sbp[lane + 64] : 0.0f;
   vm_wait<0>();  // every ordinary load lands before the first DMA is queued
 
   const uint32_t lds0 = lds_addr(lds);
-  auto issue = [&](int stage, int kb) {
+  // DMA j of this wave for K block kb into LDS stage `stage`: j < kQW moves A/B
+  // rows, j == kQW the wave's A scales
+  // (every operand but voff / soff is wave-uniform: addresses and m0 stay in SGPRs)
+  auto issue_one = [&](int stage, int kb, int j) {
     const uint32_t base = lds0 + stage * C::kStage;
     const int64_t kg = kbase + kb;  // K block in the whole problem
-    const uint8_t* ak = a_base + kg * 128;
-    const uint8_t* bk = b_base + kg * 128;
+    if (j < C::kQW) {
+      const int q = w + j * C::NW;
+      dma16((q < C::kAQ ? a_base : b_base) + kg * 128, voff[j], base + q * 1024);
+    } else {
+      dma4(s_base + kg * g.sskb * 4, soff, base + sofs);
+    }
+  };
+  auto issue = [&](int stage, int kb) {
 #pragma unroll
-    for (int j = 0; j < C::kQW; ++j)
-      dma16(is_a[j] ? ak : bk, voff[j], __builtin_amdgcn_readfirstlane(base + lofs[j]));
-    dma4(s_base + kg * g.sskb * 4, soff, __builtin_amdgcn_readfirstlane(base + sofs));
+    for (int j = 0; j <= C::kQW; ++j) issue_one(stage, kb, j);
   };
 
   v4f acc[C::kTM][C::kTN];
@@ -305,13 +312,21 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     if (s < KB) issue(s, s);
 
   // one K step on LDS stage `stage`; only the first TMV row tiles of the wave are computed
-  auto step = [&](const int kb, const int stage, auto tmv_c) {
+  // RF 1: the step refills its stage (steady state, no branches); RF 0: checked
+  auto step = [&](const int kb, const int stage, auto tmv_c, auto rf_c) {
     constexpr int TMV = decltype(tmv_c)::value;
-    const int ahead = min(C::S - 2, KB - 1 - kb);
-    vm_wait_stages<C::kLoadsPerStage>(ahead);
+    constexpr int RF = decltype(rf_c)::value;
+    if constexpr (RF == 1) {
+      vm_wait<(C::S - 2) * C::kLoadsPerStage>();
+    } else {
+      vm_wait_stages<C::kLoadsPerStage>(min(C::S - 2, KB - 1 - kb));
+    }
     barrier_only();
-    if (kb + C::S - 1 < KB) issue((stage + C::S - 1) % C::S, kb + C::S - 1);
-    if constexpr (TMV > 0) {
+    const bool refill = RF == 1 || kb + C::S - 1 < KB;
+    const int nstage = (stage + C::S - 1) % C::S, nkb = kb + C::S - 1;
+    if constexpr (TMV == 0) {
+      if (refill) issue(nstage, nkb);
+    } else {
       const uint8_t* st = lds + stage * C::kStage;
       const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? sbv0 : sbv1), kb & 63));
       v8i av[TMV];
@@ -324,12 +339,18 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
       v8i bv[C::kTN];
 #pragma unroll
       for (int tn = 0; tn < C::kTN; ++tn) bv[tn] = lds_frag(st + C::kBOff, wn * C::kWTNB + tn * 16, lane);
-      // rolling window: tile q is issued, tile q-2 is folded
+      // rolling window: tile q is issued, tile q-2 is folded.  The refill DMAs of
+      // the stage freed by the barrier are spread between the MFMAs (DMA j after
+      // MFMA j * kGap), so a wave never stalls on a burst of DMA issues.
       constexpr int NQ = TMV * C::kTN;
+      constexpr int kGap = NQ / (C::kQW + 1) > 0 ? NQ / (C::kQW + 1) : 1;
       v4f tq[3];
 #pragma unroll
       for (int q = 0; q < NQ + 2; ++q) {
         if (q < NQ) tq[q % 3] = mfma16x16x128_fp8(av[q % TMV], bv[q / TMV], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int j = 0; j <= C::kQW; ++j)
+          if (refill && (j * kGap < NQ + 1 ? j * kGap : NQ + 1) == q) issue_one(nstage, nkb, j);
         if (q >= 2) {
           const int p = q - 2;
           acc[p % TMV][p / TMV] += tq[p % 3] * s4[p % TMV];
@@ -339,10 +360,16 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   };
   // unrolled by the stage count: every LDS address is base + immediate
   auto kloop = [&](auto tmv_c) {
-    for (int kb0 = 0; kb0 < KB; kb0 += C::S) {
+    int kb0 = 0;
+    // rounds whose every step refills (kb + S - 1 < KB for the round's last step)
+    for (; kb0 + 2 * C::S - 1 <= KB; kb0 += C::S) {
+#pragma unroll
+      for (int u = 0; u < C::S; ++u) step(kb0 + u, u, tmv_c, std::integral_constant<int, 1>{});
+    }
+    for (; kb0 < KB; kb0 += C::S) {
 #pragma unroll
       for (int u = 0; u < C::S; ++u)
-        if (kb0 + u < KB) step(kb0 + u, u, tmv_c);
+        if (kb0 + u < KB) step(kb0 + u, u, tmv_c, std::integral_constant<int, 0>{});
     }
   };
   static_assert(C::kTM <= 4, "row tiles per wave");
@@ -420,67 +447,56 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
             *reinterpret_cast<const u32x4*>(ob + r * C::BNB + ch * 4);
     }
   } else {
-    // gate waves hand their tiles to the up waves with the same lanes; up waves form
-    // h = SiLU(gate) * up, then each row's 128 columns are requantised 1x128.
-    constexpr int HW = C::kWN / 2;  // waves per part along N
-    float* xg = reinterpret_cast<float*>(lds);
-    uint8_t* ob = lds + C::WM * HW * C::kTM * C::kTN * 64 * 16;
-    const int pw = wm * HW + (wn % HW);
-    if (part == 0) {
+    // Both parts stage their fp32 tiles in LDS as rows [gate 128 | up 128] (row
+    // stride kFS words: conflict-free stores).  Then each thread takes kCPI
+    // consecutive columns of one row: h = SiLU(gate) * up, the row's amax over its
+    // 128 columns (partial maxima through red), 1x128 requantisation, and 16-byte
+    // stores of the codes straight to h8.
+    constexpr int kFS = 2 * 128 + 4;
+    constexpr int kQPR = C::kQPR, kCPI = 128 / kQPR;
+    static_assert(C::BM * kFS * 4 <= C::kLds, "gate/up tile fits the pipeline LDS");
+    float* F = reinterpret_cast<float*>(lds);
 #pragma unroll
-      for (int tm = 0; tm < C::kTM; ++tm)
+    for (int tm = 0; tm < C::kTM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < C::kTN; ++tn)
-          *reinterpret_cast<v4f*>(xg + (((pw * C::kTM + tm) * C::kTN + tn) * 64 + lane) * 4) = acc[tm][tn];
-    }
+      for (int tn = 0; tn < C::kTN; ++tn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          F[(wm * C::kWTM + tm * 16 + 4 * lg + i) * kFS + part * 128 + colofs + tn * 16 + lr] = acc[tm][tn][i];
     __syncthreads();
-    if (part == 1) {
+    const int r = tid % C::BM, qc = tid / C::BM;  // row and column group of this thread
+    const bool active = qc < kQPR;
+    float h[kCPI];
+    if (active) {
+      float mx = 0.0f;
 #pragma unroll
-      for (int tm = 0; tm < C::kTM; ++tm) {
-        float mx[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int tn = 0; tn < C::kTN; ++tn) {
-          const v4f gt = *reinterpret_cast<const v4f*>(xg + (((pw * C::kTM + tm) * C::kTN + tn) * 64 + lane) * 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float h = gt[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-gt[i])) * acc[tm][tn][i];
-            acc[tm][tn][i] = h;
-            mx[i] = fmaxf(mx[i], fabsf(h));
-          }
-        }
+      for (int v = 0; v < kCPI; v += 4) {
+        const v4f gt = *reinterpret_cast<const v4f*>(F + r * kFS + qc * kCPI + v);
+        const v4f up = *reinterpret_cast<const v4f*>(F + r * kFS + 128 + qc * kCPI + v);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = mx[i];
-#pragma unroll
-          for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-          if (lr == 0) red[wn % HW][wm * C::kWTM + tm * 16 + 4 * lg + i] = v;
+          h[v + i] = gt[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-gt[i])) * up[i];
+          mx = fmaxf(mx, fabsf(h[v + i]));
         }
       }
+      red[qc][r] = mx;
     }
     __syncthreads();
-    if (part == 1) {
-      const int IB = g.N / 128;
+    if (active && rowinfo[r] < npairs) {
+      float amax = red[0][r];
 #pragma unroll
-      for (int tm = 0; tm < C::kTM; ++tm)
+      for (int k2 = 1; k2 < kQPR; ++k2) amax = fmaxf(amax, red[k2][r]);
+      const float sc = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+      uint32_t wds[kCPI / 4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rl = wm * C::kWTM + tm * 16 + 4 * lg + i;
-          float amax = red[0][rl];
+      for (int v = 0; v < kCPI / 4; ++v)
+        wds[v] = f32_to_e4m3(h[4 * v] / sc) | (f32_to_e4m3(h[4 * v + 1] / sc) << 8) |
+                 (f32_to_e4m3(h[4 * v + 2] / sc) << 16) | (f32_to_e4m3(h[4 * v + 3] / sc) << 24);
+      uint8_t* dst = g.h8 + (row0 + r) * g.N + nt * 128 + qc * kCPI;
 #pragma unroll
-          for (int k2 = 1; k2 < HW; ++k2) amax = fmaxf(amax, red[k2][rl]);
-          const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
-#pragma unroll
-          for (int tn = 0; tn < C::kTN; ++tn)
-            ob[rl * 128 + colofs + tn * 16 + lr] = (uint8_t)f32_to_e4m3(acc[tm][tn][i] / s);
-          if (colofs == 0 && lr == 0 && rowinfo[rl] < npairs) g.h_scale[(row0 + rl) * IB + nt] = s;
-        }
-    }
-    __syncthreads();
-    for (int ci = tid; ci < C::BM * 8; ci += C::kThreads) {
-      const int rl = ci >> 3, ch = ci & 7;
-      if (rowinfo[rl] < npairs)
-        *reinterpret_cast<u32x4*>(g.h8 + (row0 + rl) * g.N + nt * 128 + ch * 16) =
-            *reinterpret_cast<const u32x4*>(ob + rl * 128 + ch * 16);
+      for (int v = 0; v < kCPI / 16; ++v)
+        *reinterpret_cast<u32x4*>(dst + 16 * v) = u32x4{wds[4 * v], wds[4 * v + 1], wds[4 * v + 2], wds[4 * v + 3]};
+      if (qc == 0) g.h_scale[(row0 + r) * (g.N / 128) + nt] = sc;
     }
   }
 }
