@@ -84,7 +84,8 @@ struct Cfg {
   static constexpr int kStage = kSOff + NW * 256;     // 64 fp32 A scales per wave
   static constexpr int kLds = S * kStage;
   // g1u1 epilogue: threads per output row (each takes 128 / kQPR columns)
-  static constexpr int kQPR = kThreads / BM >= 8 ? 8 : 4;
+  static constexpr int kQPR = kThreads / BM >= 8 ? 8 : kThreads / BM;
+  static_assert(MODE != kG1U1 || (kQPR >= 1 && 128 % kQPR == 0 && 128 / kQPR % 16 == 0), "g1u1 epilogue split");
   static constexpr int kRed = kQPR > kWN ? kQPR : kWN;
   static_assert(kWTM % 16 == 0 && kWTNB % 16 == 0, "wave tile must be whole MFMA tiles");
   static_assert(kWTNB <= 128 && 128 % kWTNB == 0, "a wave's columns lie in one 128-column scale block");
@@ -172,8 +173,9 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
 
   // Tiles are (M block, N tile) pairs, N tile fastest, one per workgroup: the N
   // tiles of an M block share its A rows and run side by side; consecutive M
-  // blocks of one expert share weights.  (Remapping tiles onto XCD-contiguous
-  // ranges measured slower: weight reuse across M blocks matters more.)
+  // blocks of one expert share weights.  Workgroup b runs on XCD b % 8 (one L2
+  // each), in order of b; orders that put all readers of a tile on one XCD
+  // (contiguous ranges, persistent rounds, paired M blocks) measured slower.
   // Dense split-K: tile index = split * (M blocks * N tiles) + M block * N tiles + N tile.
   int64_t total;
   int nvalid = 0;

@@ -99,12 +99,20 @@ __global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(SortWs ws, int 
   const int e = threadIdx.x;
   if (e == 0) bad = 0;
   __syncthreads();
+  // per-chunk counts -> exclusive per-chunk offsets of expert e; loads issued in
+  // batches so that their latencies overlap
+  constexpr int kBatch = 16;
   int c = 0;
   if (e < E) {
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const int v = ws.counts[(int64_t)ch * E + e];
-      ws.counts[(int64_t)ch * E + e] = c;
-      c += v;
+    for (int ch0 = 0; ch0 < nchunks; ch0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = ch0 + i < nchunks ? ws.counts[(int64_t)(ch0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (ch0 + i < nchunks) ws.counts[(int64_t)(ch0 + i) * E + e] = c;
+        c += v[i];
+      }
     }
   }
   for (int ch = e; ch < nchunks; ch += kScanThreads)
