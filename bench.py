@@ -298,7 +298,7 @@ def bench_dense(a):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU (the layer is not sharded); "
+        print("bench.py: libmoe355 runs the layer on one GPU (it is not sharded across GPUs); "
               "run without --gpus or with --gpus 1", file=sys.stderr)
         sys.exit(2)
     res = bench_dense(a) if a.workload == "dense" else bench_moe(a)

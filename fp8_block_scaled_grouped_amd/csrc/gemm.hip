@@ -503,9 +503,12 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   }
 }
 
-// out[t, n] = bf16(sum_j y[t*k + j, n]), j ascending, fp32.
+// out[t, n] = bf16(sum_j y[t*k + j, n]), j ascending, fp32.  Writes nothing when
+// the sort flagged an invalid expert id (num_valid < 0: the pairs were not placed).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int T, int k, int H,
-                                                      uint16_t* __restrict__ out, int64_t ld_out) {
+                                                      uint16_t* __restrict__ out, int64_t ld_out,
+                                                      const int32_t* __restrict__ num_valid) {
+  if (num_valid[0] < 0) return;
   const int H8 = H / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t t = idx / H8;
@@ -773,6 +776,6 @@ extern "C" int moe_down_combine(const uint8_t* h8, const float* h_scale, const u
   if (st != MOE355_OK) return st;
   const int64_t threads = (int64_t)T * (H / 8);
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)ceil_div64(threads, 256)), dim3(256), 0, stream, g.y, T, topk, H,
-                     out, ld_out);
+                     out, ld_out, num_valid);
   return launch_status();
 }

@@ -136,7 +136,8 @@ int fp8_quant_1x128(const uint16_t* x, int64_t ld_x, int M, int K,
  * sorted_*  / num_valid as written by moe_sort with the same block_m; max_sorted
  *           is the capacity returned by moe_sort_sizes.
  * h8        e4m3 [max_sorted, I] out; h_scale fp32 [max_sorted, I/128] out.
- *           Padding rows and rows at or beyond num_valid are not written.
+ *           Padding rows and rows at or beyond num_valid are not written (nothing
+ *           is written when num_valid is -1).
  * H % 128 == 0, I % 128 == 0, block_m in {16, 32, 64, 128}; a8, w1, h8 16-byte aligned.
  */
 int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale,
@@ -161,7 +162,8 @@ int moe_down_combine_workspace(int T, int H, int topk, size_t* bytes);
  * w2        e4m3 [E, H, I]; w2_scale fp32 [E, H/128, I/128].
  * out       bf16 bits [T, H] out, row stride ld_out >= H (16-byte aligned rows).
  * workspace device memory of at least moe_down_combine_workspace() bytes.
- * Every pair of the T*topk must appear in the sorted buffer (moe_sort guarantees it).
+ * Every pair of the T*topk must appear in the sorted buffer (moe_sort guarantees it
+ * for valid ids); when num_valid is -1 (an id outside [0, E)) out is not written.
  */
 int moe_down_combine(const uint8_t* h8, const float* h_scale,
                      const uint8_t* w2, const float* w2_scale,

@@ -99,3 +99,17 @@ def test_dense_workspace_query(lib):
     assert moe355.gemm_fp8_blockscale_workspace(1, 2048, 256) == 0  # two K blocks: nothing to split
     with pytest.raises(moe355.Moe355Error):
         moe355.gemm_fp8_blockscale_workspace(1, 100, 256)
+
+
+def test_zero_rows_are_noops_without_touching_memory(lib):
+    # zero tokens / rows: OK before any pointer is looked at (all NULL here, no GPU needed)
+    L = lib
+    N = None
+    assert L.grouped_topk(N, 16, N, 0, 16, 4, 2, 4, 1, 2.5, N, N, 4, N) == 0
+    assert L.moe_sort(N, N, 4, 0, 4, 16, 16, N, N, N, N, N, 0, N) == 0
+    assert L.fp8_quant_1x128(N, 256, 0, 256, N, 256, N, 2, 1, N) == 0
+    assert L.moe_fp8_blockscale_g1u1(N, N, 2, 1, N, N, N, N, N, 0, 256, 128, 16, 4, 16, 256, N, N, N) == 0
+    assert L.moe_down_combine(N, N, N, N, N, N, N, N, 0, 256, 128, 16, 4, 16, 256, N, 256, N, 0, N) == 0
+    assert L.gemm_fp8_blockscale(N, N, 2, 1, N, N, 0, 256, 256, N, 256, N, 0, N) == 0
+    # ...but shape rules still apply
+    assert L.moe_sort(N, N, 4, 0, 4, 16, 24, N, N, N, N, N, 0, N) == -2

@@ -247,3 +247,30 @@ def test_dense_split_deterministic(m):
     c2 = m.gemm_fp8_blockscale(a8, sa, d["b"], d["b_scale"]).clone()
     torch.cuda.synchronize()
     assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+
+
+def test_invalid_expert_id_marks_num_valid_and_gemms_skip(m, tiny):
+    # an id outside [0, E) sets num_valid = -1; the grouped GEMMs then write nothing
+    cfg, x = tiny
+    for BM, T in [(16, cfg.T), (128, 3000)]:
+        ids = np.random.default_rng(BM).integers(0, cfg.E, (T, cfg.topk)).astype(np.int32)
+        ids[T // 2, 1] = cfg.E + 3
+        w = np.ones((T, cfg.topk), np.float32)
+        sid, sw, seid, nv = m.moe_sort(torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), cfg.E, BM)
+        torch.cuda.synchronize()
+        assert int(nv.item()) == -1
+    g = {k: v.to(DEV) for k, v in x.items()}
+    a8, sa = m.fp8_quant_1x128(g["hidden"])
+    ids = np.zeros((cfg.T, cfg.topk), np.int32)
+    ids[:, :] = np.arange(cfg.topk)
+    ids[0, 0] = -1
+    sid, sw, seid, nv = m.moe_sort(torch.from_numpy(ids).to(DEV), torch.ones((cfg.T, cfg.topk), device=DEV), cfg.E, 16)
+    h8 = torch.full((sid.numel(), cfg.I), 0x5A, dtype=torch.uint8, device=DEV)
+    hs = torch.full((sid.numel(), cfg.I // 128), 7.0, device=DEV)
+    m.moe_fp8_blockscale_g1u1(a8, sa, g["w1"], g["w1_scale"], sid, seid, nv, cfg.topk, 16, h8, hs)
+    out = torch.full((cfg.T, cfg.H), 3.0, dtype=torch.bfloat16, device=DEV)
+    m.moe_down_combine(h8, hs, g["w2"], g["w2_scale"], sid, sw, seid, nv, cfg.T, cfg.topk, 16, out)
+    torch.cuda.synchronize()
+    assert int(nv.item()) == -1
+    assert bool((h8 == 0x5A).all()) and bool((hs == 7.0).all())
+    assert bool((out == 3.0).all())
