@@ -375,7 +375,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     }
   };
   static_assert(C::kTM <= 4, "row tiles per wave");
-  static_assert(C::BM * C::BNB * 4 <= C::kLds, "fp32 output tile fits the pipeline LDS");
+  static_assert(C::BM * (C::BNB + 4) * 4 <= C::kLds, "padded fp32 output tile fits the pipeline LDS");
   switch (tm_live) {
     case 0: kloop(std::integral_constant<int, 0>{}); break;
     case 1: kloop(std::integral_constant<int, 1>{}); break;
@@ -388,7 +388,9 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
 
   // ---- epilogues (LDS is free again)
   if (MODE == kDense && g.splits > 1) {
-    // split-K partial: fp32 tile [BM][BNB] in LDS, then 16-byte stores into part[ks]
+    // split-K partial: fp32 tile [BM][BNB] in LDS (rows padded by 16 bytes so that
+    // rows 4 apart do not share banks), then 16-byte stores into part[ks]
+    constexpr int RS = C::BNB + 4;
     float* ob = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int tm = 0; tm < C::kTM; ++tm)
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
       for (int tn = 0; tn < C::kTN; ++tn)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          ob[(wm * C::kWTM + tm * 16 + 4 * lg + i) * C::BNB + wn * C::kWTNB + tn * 16 + lr] = acc[tm][tn][i];
+          ob[(wm * C::kWTM + tm * 16 + 4 * lg + i) * RS + wn * C::kWTNB + tn * 16 + lr] = acc[tm][tn][i];
     __syncthreads();
     constexpr int CPR = C::BNB * 4 / 16;
     float* dst = g.part + (int64_t)ks * g.M * g.N;
@@ -405,10 +407,11 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
       const int64_t m = row0 + r;
       if (m < g.M)
         *reinterpret_cast<u32x4*>(dst + m * g.N + (int64_t)nt * C::BNB + ch * 4) =
-            *reinterpret_cast<const u32x4*>(ob + r * C::BNB + ch * 4);
+            *reinterpret_cast<const u32x4*>(ob + r * RS + ch * 4);
     }
   } else if constexpr (MODE == kDense) {
-    // bf16 tile [BM][BNB] in LDS, then 16-byte row stores
+    // bf16 tile [BM][BNB] in LDS (rows padded by 16 bytes), then 16-byte row stores
+    constexpr int RS = C::BNB + 8;
     uint16_t* ob = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
     for (int tm = 0; tm < C::kTM; ++tm)
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
       for (int tn = 0; tn < C::kTN; ++tn)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          ob[(wm * C::kWTM + tm * 16 + 4 * lg + i) * C::BNB + wn * C::kWTNB + tn * 16 + lr] =
+          ob[(wm * C::kWTM + tm * 16 + 4 * lg + i) * RS + wn * C::kWTNB + tn * 16 + lr] =
               (uint16_t)f32_to_bf16(acc[tm][tn][i]);
     __syncthreads();
     constexpr int CPR = C::BNB * 2 / 16;  // 16-byte chunks per row
@@ -425,29 +428,25 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
       const int64_t m = row0 + r;
       if (m < g.M)
         *reinterpret_cast<u32x4*>(g.c + m * g.ldc + (int64_t)nt * C::BNB + ch * 8) =
-            *reinterpret_cast<const u32x4*>(ob + r * C::BNB + ch * 8);
+            *reinterpret_cast<const u32x4*>(ob + r * RS + ch * 8);
     }
   } else if constexpr (MODE == kDown) {
-    // routing-weighted fp32 tile [BM][BNB] in LDS, then 16-byte stores per pair row
-    float* ob = reinterpret_cast<float*>(lds);
+    // routing-weighted fp32 rows straight from the MFMA layout: for each of its rows
+    // a group of 16 lanes writes 64 contiguous bytes per row tile (the neighbouring
+    // column tiles complete the 128-byte lines in L2)
 #pragma unroll
     for (int tm = 0; tm < C::kTM; ++tm)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rl = wm * C::kWTM + tm * 16 + 4 * lg + i;
-        const float wgt = rowinfo[rl] < npairs ? g.sorted_w[row0 + rl] : 0.0f;
+        const int pid = rowinfo[rl];
+        if (row0 + rl < nvalid && pid < npairs) {
+          const float wgt = g.sorted_w[row0 + rl];
+          float* yr = g.y + (int64_t)pid * g.N + (int64_t)nt * C::BNB + wn * C::kWTNB + lr;
 #pragma unroll
-        for (int tn = 0; tn < C::kTN; ++tn) ob[rl * C::BNB + wn * C::kWTNB + tn * 16 + lr] = acc[tm][tn][i] * wgt;
+          for (int tn = 0; tn < C::kTN; ++tn) yr[tn * 16] = acc[tm][tn][i] * wgt;
+        }
       }
-    __syncthreads();
-    constexpr int CPR = C::BNB * 4 / 16;
-    for (int ci = tid; ci < C::BM * CPR; ci += C::kThreads) {
-      const int r = ci / CPR, ch = ci % CPR;
-      const int pid = rowinfo[r];
-      if (row0 + r < nvalid && pid < npairs)
-        *reinterpret_cast<u32x4*>(g.y + (int64_t)pid * g.N + (int64_t)nt * C::BNB + ch * 4) =
-            *reinterpret_cast<const u32x4*>(ob + r * C::BNB + ch * 4);
-    }
   } else {
     // Both parts stage their fp32 tiles in LDS as rows [gate 128 | up 128] (row
     // stride kFS words: conflict-free stores).  Then each thread takes kCPI
