@@ -41,6 +41,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// fp16 bits of x, round to nearest even (the hardware conversion)
+__device__ __forceinline__ uint32_t f32_to_f16(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// 16-bit output element: bf16 or fp16 bits of x, nearest even
+__device__ __forceinline__ uint32_t f32_to_out16(float x, bool fp16) { return fp16 ? f32_to_f16(x) : f32_to_bf16(x); }
+
 __device__ __forceinline__ float wave_max_f32(float v, int width) {
   for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;

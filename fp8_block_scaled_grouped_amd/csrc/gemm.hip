@@ -58,6 +58,7 @@ struct GemmArgs {
   float* h_scale;          // g1u1 out [max_sorted, N/128]
   float* y;                // down staging [T*topk, N] fp32
   int splits, kbs;         // dense split-K: K blocks [ks*kbs, ks*kbs+kbs) per split ks
+  int out_f16;             // dense: c holds fp16 (1) or bf16 (0) bits
   float* part;             // dense split-K partial sums [splits, M, N] fp32
 };
 
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           ob[(wm * C::kWTM + tm * 16 + 4 * lg + i) * RS + wn * C::kWTNB + tn * 16 + lr] =
-              (uint16_t)f32_to_bf16(acc[tm][tn][i]);
+              (uint16_t)f32_to_out16(acc[tm][tn][i], g.out_f16 != 0);
     __syncthreads();
     constexpr int CPR = C::BNB * 2 / 16;  // 16-byte chunks per row
     for (int ci = tid; ci < C::BM * CPR; ci += C::kThreads) {
@@ -531,12 +532,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<u32x4*>(out + t * ld_out + c8 * 8) = o;
 }
 
-// c[m, n] = bf16 of the fp32 sum of part[split, m, n] over the splits, in a fixed
+// c[m, n] = bf16 (or fp16) of the fp32 sum of part[split, m, n] over the splits, in a fixed
 // order: wave w sums splits w, w+4, w+8, ... in ascending order, then the four
 // wave sums are added in wave order.  One workgroup covers 256 columns of one
 // row; every lane keeps up to 8 loads in flight.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
-                                                            uint16_t* __restrict__ c, int64_t ldc) {
+                                                            uint16_t* __restrict__ c, int64_t ldc, int out_f16) {
   __shared__ float sh[4][256];
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int m = blockIdx.y;
@@ -566,7 +567,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     float o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = ((sh[0][lane * 4 + i] + sh[1][lane * 4 + i]) + sh[2][lane * 4 + i]) + sh[3][lane * 4 + i];
-    const uint2 r{f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16), f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16)};
+    const bool f16 = out_f16 != 0;
+    const uint2 r{f32_to_out16(o[0], f16) | (f32_to_out16(o[1], f16) << 16),
+                  f32_to_out16(o[2], f16) | (f32_to_out16(o[3], f16) << 16)};
     *reinterpret_cast<uint2*>(c + (int64_t)m * ldc + col) = r;
   }
 }
@@ -650,8 +653,9 @@ extern "C" int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes)
 
 extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb,
                                    const uint8_t* b8, const float* b_scale, int M, int N, int K, uint16_t* c,
-                                   int64_t ldc, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && ldc >= N, MOE355_EINVAL);
+                                   int64_t ldc, int out_fp16, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && ldc >= N && (out_fp16 == 0 || out_fp16 == 1), MOE355_EINVAL);
   MOE355_CHECK(K % 128 == 0 && N % 128 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
   MOE355_CHECK((int64_t)M * K < (1ll << 32) && (int64_t)N * K < (1ll << 32), MOE355_EUNSUPPORTED);
   if (M == 0 || N == 0) return MOE355_OK;
@@ -681,13 +685,14 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
   g.ldc = ldc;
   g.splits = plan.splits;
   g.kbs = plan.kbs;
+  g.out_f16 = out_fp16;
   g.part = static_cast<float*>(workspace);
   const int64_t mblocks = ceil_div64(M, plan.bm);
   const int st = plan.bnb == 128 ? launch_gemm<kDense, 128>(g, plan.bm, mblocks, stream)
                                  : launch_gemm<kDense, 256>(g, plan.bm, mblocks, stream);
   if (st != MOE355_OK || plan.splits == 1) return st;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)ceil_div64(N, 256), (unsigned)M), dim3(256), 0, stream,
-                     g.part, plan.splits, M, N, c, ldc);
+                     g.part, plan.splits, M, N, c, ldc, out_fp16);
   return launch_status();
 }
 

@@ -37,9 +37,14 @@ __device__ __forceinline__ void wave_argbest(float& v, int& i) {
 // Fast path: lane L holds the P = E/64 (rounded up) contiguous experts
 // L*P .. L*P+P-1 in registers; a group of E/n_group experts spans LPG = gsz/P
 // consecutive lanes (a power of two), so the group top-2 is a butterfly merge.
+// logit e of row x: fp32, or bf16 bits widened exactly
+__device__ __forceinline__ float load_logit(const void* x, int e, bool bf16) {
+  return bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[e]) : reinterpret_cast<const float*>(x)[e];
+}
+
 template <int P>
 __global__ __launch_bounds__(256) void grouped_topk_reg_kernel(
-    const float* __restrict__ logits, int64_t ld_logits, const float* __restrict__ bias, int T, int E,
+    const void* __restrict__ logits, int logits_bf16, int64_t ld_logits, const float* __restrict__ bias, int T, int E,
     int n_group, int topk_group, int topk, int renorm, float factor, float* __restrict__ topk_weights,
     int32_t* __restrict__ topk_ids, int64_t ld_topk, int lpg) {
   const int lane = threadIdx.x % kWave;
@@ -47,12 +52,12 @@ __global__ __launch_bounds__(256) void grouped_topk_reg_kernel(
   if (t >= T) return;  // whole wave
   const int e0 = lane * P;
   float s[P], b[P];
-  const float* x = logits + (int64_t)t * ld_logits;
+  const void* x = reinterpret_cast<const uint8_t*>(logits) + (int64_t)t * ld_logits * (logits_bf16 ? 2 : 4);
 #pragma unroll
   for (int q = 0; q < P; ++q) {
     const int e = e0 + q;
     if (e < E) {
-      const double d = 1.0 / (1.0 + exp(-(double)x[e]));
+      const double d = 1.0 / (1.0 + exp(-(double)load_logit(x, e, logits_bf16 != 0)));
       s[q] = (float)d;
       b[q] = s[q] + bias[e];
     } else {
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(256) void grouped_topk_reg_kernel(
 
 // General path (any group shape): scores in LDS, group top-2 by a scan per group.
 __global__ __launch_bounds__(256) void grouped_topk_kernel(
-    const float* __restrict__ logits, int64_t ld_logits, const float* __restrict__ bias, int T, int E,
+    const void* __restrict__ logits, int logits_bf16, int64_t ld_logits, const float* __restrict__ bias, int T, int E,
     int n_group, int topk_group, int topk, int renorm, float factor, float* __restrict__ topk_weights,
     int32_t* __restrict__ topk_ids, int64_t ld_topk) {
   __shared__ float s_sh[kTokPerBlock][kMaxE];
@@ -143,9 +148,9 @@ __global__ __launch_bounds__(256) void grouped_topk_kernel(
 
   // scores: fl32 of the binary64 logistic, then the biased score in fp32
   if (live) {
-    const float* x = logits + (int64_t)t * ld_logits;
+    const void* x = reinterpret_cast<const uint8_t*>(logits) + (int64_t)t * ld_logits * (logits_bf16 ? 2 : 4);
     for (int e = lane; e < E; e += kWave) {
-      const double d = 1.0 / (1.0 + exp(-(double)x[e]));
+      const double d = 1.0 / (1.0 + exp(-(double)load_logit(x, e, logits_bf16 != 0)));
       const float s = (float)d;
       s_sh[w][e] = s;
       b_sh[w][e] = s + bias[e];
@@ -223,10 +228,11 @@ __global__ __launch_bounds__(256) void grouped_topk_kernel(
 
 using namespace moe355;
 
-extern "C" int grouped_topk(const float* logits, int64_t ld_logits, const float* bias, int T, int E,
+extern "C" int grouped_topk(const void* logits, int logits_bf16, int64_t ld_logits, const float* bias, int T, int E,
                             int n_group, int topk_group, int topk, int renorm, float routed_scaling_factor,
                             float* topk_weights, int32_t* topk_ids, int64_t ld_topk, hipStream_t stream) {
   MOE355_CHECK(T >= 0 && E > 0 && n_group > 0 && topk_group > 0 && topk > 0, MOE355_EINVAL);
+  MOE355_CHECK(logits_bf16 == 0 || logits_bf16 == 1, MOE355_EINVAL);
   MOE355_CHECK(ld_logits >= E && ld_topk >= topk, MOE355_EINVAL);
   MOE355_CHECK(E <= kMaxE && n_group <= 64 && E % n_group == 0 && E / n_group >= 2, MOE355_EUNSUPPORTED);
   MOE355_CHECK(topk_group <= n_group && topk <= 32 && topk <= topk_group * (E / n_group), MOE355_EUNSUPPORTED);
@@ -240,7 +246,7 @@ extern "C" int grouped_topk(const float* logits, int64_t ld_logits, const float*
 #define MOE355_TOPK_REG(PP)                                                                                         \
   case PP:                                                                                                          \
     hipLaunchKernelGGL(grouped_topk_reg_kernel<PP>, dim3(blocks), dim3(kTokPerBlock * kWave), 0, stream, logits,    \
-                       ld_logits, bias, T, E, n_group, topk_group, topk, renorm, routed_scaling_factor,           \
+                       logits_bf16, ld_logits, bias, T, E, n_group, topk_group, topk, renorm, routed_scaling_factor,           \
                        topk_weights, topk_ids, ld_topk, lpg);                                                    \
     return launch_status();
     switch (P) {
@@ -253,8 +259,8 @@ extern "C" int grouped_topk(const float* logits, int64_t ld_logits, const float*
     }
 #undef MOE355_TOPK_REG
   }
-  hipLaunchKernelGGL(grouped_topk_kernel, dim3(blocks), dim3(kTokPerBlock * kWave), 0, stream, logits, ld_logits,
-                     bias, T, E, n_group, topk_group, topk, renorm, routed_scaling_factor, topk_weights, topk_ids,
+  hipLaunchKernelGGL(grouped_topk_kernel, dim3(blocks), dim3(kTokPerBlock * kWave), 0, stream, logits, logits_bf16,
+                     ld_logits, bias, T, E, n_group, topk_group, topk, renorm, routed_scaling_factor, topk_weights, topk_ids,
                      ld_topk);
   return launch_status();
 }

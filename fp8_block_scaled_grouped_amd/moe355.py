@@ -21,7 +21,7 @@ _P64, _PSZ = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)
 
 _SIGNATURES = {
     "moe355_strerror": ([_i32], ctypes.c_char_p),
-    "grouped_topk": ([_vp, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _i64, _vp], _i32),
+    "grouped_topk": ([_vp, _i32, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _i64, _vp], _i32),
     "moe_sort_sizes": ([_i32, _i32, _i32, _i32, _P64, _P64, _PSZ], _i32),
     "moe_sort": ([_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "fp8_quant_1x128": ([_vp, _i64, _i32, _i32, _vp, _i64, _vp, _i64, _i64, _vp], _i32),
@@ -31,7 +31,8 @@ _SIGNATURES = {
     "moe_down_combine": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _vp,
                           _i64, _vp, _sz, _vp], _i32),
     "gemm_fp8_blockscale_workspace": ([_i32, _i32, _i32, _PSZ], _i32),
-    "gemm_fp8_blockscale": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _vp, _sz, _vp], _i32),
+    "gemm_fp8_blockscale": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _vp, _sz, _vp],
+                            _i32),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -91,9 +92,12 @@ def grouped_topk(logits, bias, n_group, topk_group, topk, renorm, routed_scaling
                  topk_weights=None, topk_ids=None):
     """Biased grouped top-k.  Returns (topk_weights fp32 [T, k], topk_ids int32 [T, k]).
 
-    Outputs may be passed in as row-strided views (same row stride for both).
+    logits: fp32 or bf16 [T, E].  Outputs may be passed in as row-strided views (same
+    row stride for both).
     """
-    _dev(logits, torch.float32, "logits")
+    if logits.dtype != torch.bfloat16:
+        _dev(logits, torch.float32, "logits")
+    _dev(logits, logits.dtype, "logits")
     _dev(bias, torch.float32, "bias")
     T, E = logits.shape
     if topk_weights is None:
@@ -103,7 +107,8 @@ def grouped_topk(logits, bias, n_group, topk_group, topk, renorm, routed_scaling
     ld = _rows(topk_weights, "topk_weights")
     if _rows(topk_ids, "topk_ids") != ld:
         raise ValueError("topk_weights and topk_ids must share a row stride")
-    _check(lib().grouped_topk(_ptr(logits), _rows(logits, "logits"), _ptr(bias.contiguous()), T, E, n_group,
+    _check(lib().grouped_topk(_ptr(logits), int(logits.dtype == torch.bfloat16), _rows(logits, "logits"),
+                              _ptr(bias.contiguous()), T, E, n_group,
                               topk_group, topk, int(bool(renorm)), float(routed_scaling_factor),
                               _ptr(topk_weights), _ptr(topk_ids), ld, _stream()))
     return topk_weights, topk_ids
@@ -217,8 +222,10 @@ def gemm_fp8_blockscale_workspace(M, N, K):
     return b.value
 
 
-def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row", workspace=None):
-    """a8 e4m3 [M, K] (1x128 scales), b8 e4m3 [N, K] (128x128 scales) -> bf16 [M, N].
+def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row", workspace=None,
+                        out_dtype=torch.bfloat16):
+    """a8 e4m3 [M, K] (1x128 scales), b8 e4m3 [N, K] (128x128 scales) -> [M, N] in out_dtype
+    (bf16 or fp16; taken from c when c is given).
 
     workspace: None allocates what gemm_fp8_blockscale_workspace asks for; False runs
     without workspace (no split-K); or a device uint8 tensor.
@@ -228,14 +235,16 @@ def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row", wo
     M, K = a8.shape
     N = b8.shape[0]
     if c is None:
-        c = torch.empty((M, N), dtype=torch.bfloat16, device=a8.device)
+        c = torch.empty((M, N), dtype=out_dtype, device=a8.device)
+    if c.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("c must be bf16 or fp16, got %s" % c.dtype)
     if workspace is None:
         n = gemm_fp8_blockscale_workspace(M, N, K)
         workspace = torch.empty(n, dtype=torch.uint8, device=a8.device) if n else False
     ws_ptr, ws_n = (None, 0) if workspace is False else (_ptr(workspace), workspace.numel())
     ssm, sskb = _scale_strides(a_scale, M, K, scale_layout)
     _check(lib().gemm_fp8_blockscale(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(b8), _ptr(b_scale), M, N, K, _ptr(c),
-                                     _rows(c, "c"), ws_ptr, ws_n, _stream()))
+                                     _rows(c, "c"), int(c.dtype == torch.float16), ws_ptr, ws_n, _stream()))
     return c
 
 

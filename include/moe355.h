@@ -59,14 +59,15 @@ const char* moe355_strerror(int status);
  *   topk_weights[t, j]    = s of that expert; if renorm: divided by the fp32
  *                           left-to-right sum of the row; then * routed_scaling_factor.
  *
- * logits        fp32 [T, E], row stride ld_logits >= E.
+ * logits        [T, E] router logits, row stride ld_logits >= E (elements): fp32, or
+ *               bf16 bits when logits_bf16 is 1 (each widened exactly to fp32 first).
  * bias          fp32 [E] (the correction bias).
  * topk_weights  fp32 [T, topk] out, row stride ld_topk >= topk.
  * topk_ids      int32 [T, topk] out, same row stride ld_topk.
  * Supported: 1 <= E <= 1024, E % n_group == 0, E/n_group >= 2, n_group <= 64,
  *            1 <= topk_group <= n_group, 1 <= topk <= min(32, topk_group*E/n_group).
  */
-int grouped_topk(const float* logits, int64_t ld_logits, const float* bias,
+int grouped_topk(const void* logits, int logits_bf16, int64_t ld_logits, const float* bias,
                  int T, int E, int n_group, int topk_group, int topk,
                  int renorm, float routed_scaling_factor,
                  float* topk_weights, int32_t* topk_ids, int64_t ld_topk,
@@ -183,7 +184,9 @@ int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes);
  *   c[m,n] = bf16( sum_kb a_scale(m,kb) * b_scale[n/128, kb] * sum_{k in kb} a8[m,k] * b8[n,k] )
  * a8       e4m3 [M, K] (row stride K); a_scale(m,kb) = a_scale[m*sstride_m + kb*sstride_kb].
  * b8       e4m3 [N, K] (row stride K); b_scale fp32 [N/128, K/128].
- * c        bf16 bits [M, N] out, row stride ldc >= N (16-byte aligned rows).
+ * c        [M, N] out, row stride ldc >= N (16-byte aligned rows): bf16 bits, or fp16
+ *          bits when out_fp16 is 1 (the pages' linear layer offers both output types);
+ *          round to nearest even either way.
  * workspace device memory of gemm_fp8_blockscale_workspace() bytes, or NULL / 0: small M
  *          then splits K over more workgroups, keeps fp32 partial sums there and adds them
  *          in a fixed order (deterministic); without it one workgroup per output
@@ -193,7 +196,7 @@ int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes);
 int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale,
                         int64_t sstride_m, int64_t sstride_kb,
                         const uint8_t* b8, const float* b_scale,
-                        int M, int N, int K, uint16_t* c, int64_t ldc,
+                        int M, int N, int K, uint16_t* c, int64_t ldc, int out_fp16,
                         void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 

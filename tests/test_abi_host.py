@@ -62,18 +62,21 @@ def _p(v=16):
 def test_invalid_arguments_return_codes(lib):
     L = lib
     # grouped_topk: E % n_group != 0 -> EUNSUPPORTED; ld_topk < topk -> EINVAL; null -> EINVAL
-    assert L.grouped_topk(_p(), 16, _p(), 4, 16, 3, 2, 4, 1, 1.0, _p(), _p(), 4, None) == -2
-    assert L.grouped_topk(_p(), 16, _p(), 4, 16, 4, 2, 4, 1, 1.0, _p(), _p(), 3, None) == -1
-    assert L.grouped_topk(None, 16, _p(), 4, 16, 4, 2, 4, 1, 1.0, _p(), _p(), 4, None) == -1
-    assert L.grouped_topk(_p(), 16, _p(), 4, 16, 4, 2, 9, 1, 1.0, _p(), _p(), 9, None) == -2   # topk > tg*E/G
-    assert L.grouped_topk(_p(), 16, _p(), 0, 16, 4, 2, 4, 1, 1.0, None, None, 4, None) == 0    # T = 0 no-op
+    assert L.grouped_topk(_p(), 0, 16, _p(), 4, 16, 3, 2, 4, 1, 1.0, _p(), _p(), 4, None) == -2
+    assert L.grouped_topk(_p(), 0, 16, _p(), 4, 16, 4, 2, 4, 1, 1.0, _p(), _p(), 3, None) == -1
+    assert L.grouped_topk(None, 0, 16, _p(), 4, 16, 4, 2, 4, 1, 1.0, _p(), _p(), 4, None) == -1
+    assert L.grouped_topk(_p(), 0, 16, _p(), 4, 16, 4, 2, 9, 1, 1.0, _p(), _p(), 9, None) == -2   # topk > tg*E/G
+    assert L.grouped_topk(_p(), 0, 16, _p(), 0, 16, 4, 2, 4, 1, 1.0, None, None, 4, None) == 0    # T = 0 no-op
     # quant: K % 128 -> EUNSUPPORTED; misaligned -> EMISALIGNED; ld < K -> EINVAL
     assert L.fp8_quant_1x128(_p(), 200, 4, 200, _p(), 200, _p(), 2, 1, None) == -2
     assert L.fp8_quant_1x128(_p(8), 256, 4, 256, _p(), 256, _p(), 2, 1, None) == -3
     assert L.fp8_quant_1x128(_p(), 128, 4, 256, _p(), 256, _p(), 2, 1, None) == -1
     # dense GEMM: N % 128 -> EUNSUPPORTED; ldc < N -> EINVAL
-    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 100, 256, _p(), 100, None, 0, None) == -2
-    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 64, None, 0, None) == -1
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 100, 256, _p(), 100, 0, None, 0, None) == -2
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 64, 0, None, 0, None) == -1
+    # output type flag must be 0 or 1; logits type flag likewise
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 128, 2, None, 0, None) == -1
+    assert L.grouped_topk(_p(), 2, 16, _p(), 4, 16, 4, 2, 4, 1, 1.0, _p(), _p(), 4, None) == -1
     # sort: workspace too small -> EINVAL; bad block_m -> EUNSUPPORTED
     assert L.moe_sort(_p(), _p(), 4, 16, 4, 16, 16, _p(), _p(), _p(), _p(), _p(), 1, None) == -1
     assert L.moe_sort(_p(), _p(), 4, 16, 4, 16, 24, _p(), _p(), _p(), _p(), _p(), 1 << 20, None) == -2
@@ -105,11 +108,11 @@ def test_zero_rows_are_noops_without_touching_memory(lib):
     # zero tokens / rows: OK before any pointer is looked at (all NULL here, no GPU needed)
     L = lib
     N = None
-    assert L.grouped_topk(N, 16, N, 0, 16, 4, 2, 4, 1, 2.5, N, N, 4, N) == 0
+    assert L.grouped_topk(N, 0, 16, N, 0, 16, 4, 2, 4, 1, 2.5, N, N, 4, N) == 0
     assert L.moe_sort(N, N, 4, 0, 4, 16, 16, N, N, N, N, N, 0, N) == 0
     assert L.fp8_quant_1x128(N, 256, 0, 256, N, 256, N, 2, 1, N) == 0
     assert L.moe_fp8_blockscale_g1u1(N, N, 2, 1, N, N, N, N, N, 0, 256, 128, 16, 4, 16, 256, N, N, N) == 0
     assert L.moe_down_combine(N, N, N, N, N, N, N, N, 0, 256, 128, 16, 4, 16, 256, N, 256, N, 0, N) == 0
-    assert L.gemm_fp8_blockscale(N, N, 2, 1, N, N, 0, 256, 256, N, 256, N, 0, N) == 0
+    assert L.gemm_fp8_blockscale(N, N, 2, 1, N, N, 0, 256, 256, N, 256, 0, N, 0, N) == 0
     # ...but shape rules still apply
     assert L.moe_sort(N, N, 4, 0, 4, 16, 24, N, N, N, N, N, 0, N) == -2

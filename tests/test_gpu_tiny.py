@@ -274,3 +274,33 @@ def test_invalid_expert_id_marks_num_valid_and_gemms_skip(m, tiny):
     assert int(nv.item()) == -1
     assert bool((h8 == 0x5A).all()) and bool((hs == 7.0).all())
     assert bool((out == 3.0).all())
+
+
+@pytest.mark.parametrize("T,E,G,tg,k", [(64, 256, 8, 4, 8), (9, 96, 4, 2, 6), (4096, 256, 8, 4, 8)])
+def test_topk_bf16_logits_bitexact(m, T, E, G, tg, k):
+    # bf16 router logits: the oracle routes their exact fp32 values (bf16 makes ties common)
+    g = torch.Generator().manual_seed(T + E)
+    logits = torch.randn((T, E), generator=g).to(torch.bfloat16)
+    bias = torch.randn((E,), generator=g) * 0.1
+    w, ids = m.grouped_topk(logits.to(DEV), bias.to(DEV), G, tg, k, True, 2.5)
+    torch.cuda.synchronize()
+    wr, ir = oracle.routing.grouped_topk(logits.float().numpy(), bias.numpy(), G, tg, k, True, 2.5)
+    assert np.array_equal(ids.cpu().numpy(), ir)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), wr.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 2048, 7168), (37, 384, 512), (300, 256, 1024)])
+def test_dense_fp16_output(m, M, N, K):
+    from fp8_block_scaled_grouped_amd import inputs
+    d = inputs.make_dense_inputs(M, N, K, "cpu", seed=M + 3 * N)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(d["a"]))
+    c = m.gemm_fp8_blockscale(torch.from_numpy(a8).to(DEV), torch.from_numpy(sa).to(DEV), d["b"].to(DEV),
+                              d["b_scale"].to(DEV), out_dtype=torch.float16)
+    cb = m.gemm_fp8_blockscale(torch.from_numpy(a8).to(DEV), torch.from_numpy(sa).to(DEV), d["b"].to(DEV),
+                               d["b_scale"].to(DEV))
+    torch.cuda.synchronize()
+    assert c.dtype == torch.float16
+    ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
+    assert_rel_max(c.float().cpu().numpy().astype(np.float64), ref, what="dense fp16 %dx%dx%d" % (M, N, K))
+    # same fp32 result rounded two ways: fp16 and bf16 agree to bf16 precision
+    assert torch.allclose(c.float(), cb.float(), rtol=2 ** -7, atol=1e-3)
