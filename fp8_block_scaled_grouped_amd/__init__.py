@@ -13,6 +13,7 @@ from .moe355 import (  # noqa: F401
     gemm_fp8_blockscale_workspace,
     grouped_topk,
     lib,
+    moe_block_m,
     moe_down_combine,
     moe_down_combine_workspace,
     moe_fp8_blockscale_g1u1,

@@ -272,6 +272,17 @@ extern "C" int moe_sort_sizes(int T, int topk, int E, int block_m, int64_t* max_
   return MOE355_OK;
 }
 
+// M tile of the grouped GEMMs by the expected pairs per expert, T*topk/E (uniform
+// routing), from a sweep of the whole layer on MI355X with V3 shapes: weight
+// streaming wants the smallest tile while experts hold a few rows, the 128-row
+// 8-wave tile wins once an expert holds a few dozen.
+extern "C" int moe_block_m(int T, int topk, int E, int* block_m) {
+  MOE355_CHECK(T >= 0 && topk > 0 && E > 0 && block_m, MOE355_EINVAL);
+  const int64_t pairs = (int64_t)T * topk;
+  *block_m = pairs < 4ll * E ? 16 : pairs < 16ll * E ? 32 : 128;
+  return MOE355_OK;
+}
+
 extern "C" int moe_sort(const int32_t* topk_ids, const float* topk_weights, int64_t ld_topk, int T, int topk, int E,
                         int block_m, int32_t* sorted_ids, float* sorted_weights, int32_t* sorted_expert_ids,
                         int32_t* num_valid, void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -23,6 +23,7 @@ _SIGNATURES = {
     "moe355_strerror": ([_i32], ctypes.c_char_p),
     "grouped_topk": ([_vp, _i32, _i64, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _i64, _vp], _i32),
     "moe_sort_sizes": ([_i32, _i32, _i32, _i32, _P64, _P64, _PSZ], _i32),
+    "moe_block_m": ([_i32, _i32, _i32, ctypes.POINTER(ctypes.c_int)], _i32),
     "moe_sort": ([_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "fp8_quant_1x128": ([_vp, _i64, _i32, _i32, _vp, _i64, _vp, _i64, _i64, _vp], _i32),
     "moe_fp8_blockscale_g1u1": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -120,6 +121,13 @@ def moe_sort_sizes(T, topk, E, block_m):
     ms, mb, ws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
     _check(lib().moe_sort_sizes(T, topk, E, block_m, ctypes.byref(ms), ctypes.byref(mb), ctypes.byref(ws)))
     return ms.value, mb.value, ws.value
+
+
+def moe_block_m(T, topk, E):
+    """Tuned M tile of the grouped GEMMs for this size (host-only)."""
+    b = ctypes.c_int()
+    _check(lib().moe_block_m(T, topk, E, ctypes.byref(b)))
+    return b.value
 
 
 def moe_sort(topk_ids, topk_weights, E, block_m, out=None, workspace=None):
@@ -260,7 +268,9 @@ class MoELayer:
     def __init__(self, cfg, bias, w1, w1_scale, w2, w2_scale, T=None, block_m=None, scale_layout="row"):
         self.cfg = cfg
         self.T = cfg.T if T is None else T
-        self.block_m = cfg.block_m if block_m is None else block_m
+        if block_m is None:
+            block_m = cfg.block_m if cfg.block_m else moe_block_m(self.T, cfg.topk, cfg.E)
+        self.block_m = block_m
         self.bias, self.w1, self.w1_scale, self.w2, self.w2_scale = bias, w1, w1_scale, w2, w2_scale
         self.scale_layout = scale_layout
         dev = w1.device

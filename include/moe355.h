@@ -85,6 +85,14 @@ int moe_sort_sizes(int T, int topk, int E, int block_m,
                    int64_t* max_sorted, int64_t* max_blocks, size_t* workspace_bytes);
 
 /*
+ * Host-only tile choice for moe_sort and the grouped GEMMs (no GPU access): the
+ * block_m that measured fastest for the whole layer at this size, from the expected
+ * pairs per expert p = T*topk/E:  p < 4 -> 16;  p < 16 -> 32;  else 128.
+ * Routing that concentrates pairs on few experts favours a larger block_m than this.
+ */
+int moe_block_m(int T, int topk, int E, int* block_m);
+
+/*
  * MoE align/sort ("Complete MoE Implementation" / "MoE Sorting": token-expert
  * pairs bucketed per expert for the grouped GEMM).  Pairs are flattened as
  * p = t*topk + j.  For experts in ascending order, expert e's pairs occupy a

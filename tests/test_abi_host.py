@@ -116,3 +116,14 @@ def test_zero_rows_are_noops_without_touching_memory(lib):
     assert L.gemm_fp8_blockscale(N, N, 2, 1, N, N, 0, 256, 256, N, 256, 0, N, 0, N) == 0
     # ...but shape rules still apply
     assert L.moe_sort(N, N, 4, 0, 4, 16, 24, N, N, N, N, N, 0, N) == -2
+
+
+def test_block_m_table(lib):
+    from fp8_block_scaled_grouped_amd import moe355
+    # V3 (E 256, top-8): decode-sized batches stream weights with 16-row tiles,
+    # a few hundred tokens use 32, prefill sizes the 128-row tile
+    assert [moe355.moe_block_m(T, 8, 256) for T in (1, 64, 127, 128, 256, 511, 512, 8192)] == \
+        [16, 16, 16, 32, 32, 32, 128, 128]
+    assert moe355.moe_block_m(0, 8, 256) == 16
+    with pytest.raises(moe355.Moe355Error):
+        moe355.moe_block_m(1, 0, 256)
