@@ -57,6 +57,7 @@ struct GemmArgs {
   uint8_t* h8;             // g1u1 out [max_sorted, N]
   float* h_scale;          // g1u1 out [max_sorted, N/128]
   float* y;                // down staging [T*topk, N] fp32
+  const float* smooth;     // g1u1: optional per-expert channel factors for h [E, N] (fc2 smoothing)
   int splits, kbs;         // dense split-K: K blocks [ks*kbs, ks*kbs+kbs) per split ks
   int out_f16;             // dense: c holds fp16 (1) or bf16 (0) bits
   float* part;             // dense split-K partial sums [splits, M, N] fp32
@@ -471,13 +472,17 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     float h[kCPI];
     if (active) {
       float mx = 0.0f;
+      // fc2 smoothing factors of this expert's columns (uniform branch: pointer or none)
+      const float* sm = g.smooth ? g.smooth + (int64_t)expert * g.N + nt * 128 + qc * kCPI : nullptr;
 #pragma unroll
       for (int v = 0; v < kCPI; v += 4) {
         const v4f gt = *reinterpret_cast<const v4f*>(F + r * kFS + qc * kCPI + v);
         const v4f up = *reinterpret_cast<const v4f*>(F + r * kFS + 128 + qc * kCPI + v);
+        const v4f f = sm ? *reinterpret_cast<const v4f*>(sm + v) : v4f{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           h[v + i] = gt[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-gt[i])) * up[i];
+          if (sm) h[v + i] = h[v + i] * f[i];
           mx = fmaxf(mx, fabsf(h[v + i]));
         }
       }
@@ -700,7 +705,7 @@ extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, 
                                        const uint8_t* w1, const float* w1_scale, const int32_t* sorted_ids,
                                        const int32_t* sorted_expert_ids, const int32_t* num_valid, int T, int H,
                                        int I, int E, int topk, int block_m, int64_t max_sorted, uint8_t* h8,
-                                       float* h_scale, hipStream_t stream) {
+                                       float* h_scale, const float* fc2_smooth_scale, hipStream_t stream) {
   MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0, MOE355_EINVAL);
   MOE355_CHECK(H % 128 == 0 && I % 128 == 0 && H <= 16384 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
   MOE355_CHECK((int64_t)T * H < (1ll << 32) && (int64_t)2 * I * H < (1ll << 32), MOE355_EUNSUPPORTED);
@@ -711,12 +716,14 @@ extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, 
                MOE355_EINVAL);
   MOE355_CHECK(sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
   MOE355_CHECK(aligned16(a8) && aligned16(w1) && aligned16(h8), MOE355_EMISALIGNED);
-  MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0, MOE355_EMISALIGNED);
+  MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0 && aligned16(fc2_smooth_scale),
+               MOE355_EMISALIGNED);
   GemmArgs g{};
   g.a = a8;
   g.a_scale = a_scale;
   g.ssm = sstride_m;
   g.sskb = sstride_kb;
+  g.smooth = fc2_smooth_scale;
   g.b = w1;
   g.b_scale = w1_scale;
   g.sorted_ids = sorted_ids;

@@ -27,7 +27,7 @@ _SIGNATURES = {
     "moe_sort": ([_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "fp8_quant_1x128": ([_vp, _i64, _i32, _i32, _vp, _i64, _vp, _i64, _i64, _vp], _i32),
     "moe_fp8_blockscale_g1u1": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
-                                 _i64, _vp, _vp, _vp], _i32),
+                                 _i64, _vp, _vp, _vp, _vp], _i32),
     "moe_down_combine_workspace": ([_i32, _i32, _i32, _PSZ], _i32),
     "moe_down_combine": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _vp,
                           _i64, _vp, _sz, _vp], _i32),
@@ -180,8 +180,11 @@ def _scale_strides(a_scale, T, H, scale_layout):
 
 # ----------------------------------------------------------------- grouped GEMMs
 def moe_fp8_blockscale_g1u1(a8, a_scale, w1, w1_scale, sorted_ids, sorted_expert_ids, num_valid, topk, block_m,
-                            h8=None, h_scale=None, scale_layout="row"):
-    """Gate/up grouped GEMM + SiLU*up + 1x128 requant.  Returns (h8 [max_sorted, I], h_scale [max_sorted, I/128])."""
+                            h8=None, h_scale=None, scale_layout="row", fc2_smooth_scale=None):
+    """Gate/up grouped GEMM + SiLU*up (* fc2_smooth_scale [E, I] if given) + 1x128 requant.
+
+    Returns (h8 [max_sorted, I], h_scale [max_sorted, I/128]).
+    """
     _dev(a8, torch.uint8, "a8")
     _dev(w1, torch.uint8, "w1")
     T, H = a8.shape
@@ -195,7 +198,10 @@ def moe_fp8_blockscale_g1u1(a8, a_scale, w1, w1_scale, sorted_ids, sorted_expert
     ssm, sskb = _scale_strides(a_scale, T, H, scale_layout)
     _check(lib().moe_fp8_blockscale_g1u1(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(w1), _ptr(w1_scale),
                                          _ptr(sorted_ids), _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E,
-                                         topk, block_m, ms, _ptr(h8), _ptr(h_scale), _stream()))
+                                         topk, block_m, ms, _ptr(h8), _ptr(h_scale),
+                                         _ptr(None if fc2_smooth_scale is None else
+                                              _dev(fc2_smooth_scale, torch.float32, "fc2_smooth_scale").contiguous()),
+                                         _stream()))
     return h8, h_scale
 
 
@@ -265,7 +271,8 @@ class MoELayer:
     moe_down_combine on the current stream.
     """
 
-    def __init__(self, cfg, bias, w1, w1_scale, w2, w2_scale, T=None, block_m=None, scale_layout="row"):
+    def __init__(self, cfg, bias, w1, w1_scale, w2, w2_scale, T=None, block_m=None, scale_layout="row",
+                 fc2_smooth_scale=None):
         self.cfg = cfg
         self.T = cfg.T if T is None else T
         if block_m is None:
@@ -273,6 +280,7 @@ class MoELayer:
         self.block_m = block_m
         self.bias, self.w1, self.w1_scale, self.w2, self.w2_scale = bias, w1, w1_scale, w2, w2_scale
         self.scale_layout = scale_layout
+        self.fc2_smooth_scale = fc2_smooth_scale
         dev = w1.device
         T, H, I, E, k = self.T, cfg.H, cfg.I, cfg.E, cfg.topk
         ms, mb, wsb = moe_sort_sizes(T, k, E, self.block_m)
@@ -299,7 +307,7 @@ class MoELayer:
         sid, sw, seid, nv = moe_sort(self.topk_ids, self.topk_w, c.E, self.block_m, self.sort_out, self.sort_ws)
         fp8_quant_1x128(hidden, self.a8, self.a_scale, self.scale_layout)
         moe_fp8_blockscale_g1u1(self.a8, self.a_scale, self.w1, self.w1_scale, sid, seid, nv, c.topk, self.block_m,
-                                self.h8, self.h_scale, self.scale_layout)
+                                self.h8, self.h_scale, self.scale_layout, self.fc2_smooth_scale)
         moe_down_combine(self.h8, self.h_scale, self.w2, self.w2_scale, sid, sw, seid, nv, self.T, c.topk,
                          self.block_m, self.out, self.down_ws)
         return self.out

@@ -139,12 +139,18 @@ int fp8_quant_1x128(const uint16_t* x, int64_t ld_x, int M, int K,
  * token t = sorted_ids[r] / topk, expert e = sorted_expert_ids[r / block_m]:
  *   acc[n] = sum_kb a_scale(t,kb) * w1_scale[e, n/128, kb] * sum_{k in kb} a8[t,k] * w1[e,n,k]
  *   h[i]   = SiLU(acc[i]) * acc[I+i],  i < I            (fp32)
+ *   h[i]   = fl32(h[i] * fc2_smooth_scale[e, i])         (only when fc2_smooth_scale is given)
  *   h8[r, :], h_scale[r, :] = 1x128 quantisation of h (same rule as fp8_quant_1x128)
  * a8        e4m3 [T, H] (row stride H); a_scale(t,kb) = a_scale[t*sstride_m + kb*sstride_kb].
  * w1        e4m3 [E, 2I, H]: rows [0, I) gate, [I, 2I) up;  w1_scale fp32 [E, 2I/128, H/128].
  * sorted_*  / num_valid as written by moe_sort with the same block_m; max_sorted
  *           is the capacity returned by moe_sort_sizes.
  * h8        e4m3 [max_sorted, I] out; h_scale fp32 [max_sorted, I/128] out.
+ * fc2_smooth_scale  fp32 [E, I] (16-byte aligned) or NULL: per-expert channel factors
+ *           applied to h before its quantisation (the pages pass an optional
+ *           fc2_smooth_scale to the fused MoE call without defining it; this is the
+ *           smoothing reading: the down projection's input is scaled per channel and the
+ *           caller folds the inverse factors into w2).
  *           Padding rows and rows at or beyond num_valid are not written (nothing
  *           is written when num_valid is -1).
  * H % 128 == 0, I % 128 == 0, block_m in {16, 32, 64, 128}; a8, w1, h8 16-byte aligned.
@@ -155,7 +161,8 @@ int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale,
                             const int32_t* sorted_ids, const int32_t* sorted_expert_ids,
                             const int32_t* num_valid,
                             int T, int H, int I, int E, int topk, int block_m, int64_t max_sorted,
-                            uint8_t* h8, float* h_scale, hipStream_t stream);
+                            uint8_t* h8, float* h_scale, const float* fc2_smooth_scale,
+                            hipStream_t stream);
 
 /* Host-only workspace query for moe_down_combine (no GPU access). */
 int moe_down_combine_workspace(int T, int H, int topk, size_t* bytes);

@@ -16,7 +16,10 @@ Readings taken where the page hides the step inside its fused kernel:
     binary64, is requantised with the same dynamic 1x128 rule as the
     activations before the down projection (both products on FP8);
   * the routing weight multiplies each pair's down-projection output, and a
-    token's k weighted outputs are summed in ascending j, in binary64.
+    token's k weighted outputs are summed in ascending j, in binary64;
+  * the optional fc2_smooth_scale (passed to the fused call, never defined on
+    the page) is read as per-expert channel factors [E, I] on h before its
+    requantisation: h_i = fl32(h_i * s[e, i]), an fp32 product.
 """
 import numpy as np
 
@@ -31,14 +34,23 @@ def silu_mul_f32(g, u):
         return (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
 
 
-def expert_ffn_h(a8_rows, a_scale_rows, w1_e, w1_scale_e):
+def smooth_f32(h, smooth_e):
+    """fl32(h_i * s_i) per channel (fp32 operands; the product is exact in binary64)."""
+    if smooth_e is None:
+        return h
+    prod = np.asarray(h, np.float32).astype(np.float64) * np.asarray(smooth_e, np.float32).astype(np.float64)
+    return prod.astype(np.float32)
+
+
+def expert_ffn_h(a8_rows, a_scale_rows, w1_e, w1_scale_e, smooth_e=None):
     """Gate/up GEMM for rows of one expert -> (h float32 [R, I], acc float64 [R, 2I])."""
     acc = gemm.gemm_blockscale(a8_rows, a_scale_rows, w1_e, w1_scale_e)
     I = acc.shape[1] // 2
-    return silu_mul_f32(acc[:, :I], acc[:, I:]), acc
+    return smooth_f32(silu_mul_f32(acc[:, :I], acc[:, I:]), smooth_e), acc
 
 
-def g1u1(a8, a_scale, w1, w1_scale, sorted_ids, sorted_expert_ids, num_valid, topk, block_m):
+def g1u1(a8, a_scale, w1, w1_scale, sorted_ids, sorted_expert_ids, num_valid, topk, block_m,
+         fc2_smooth_scale=None):
     """Gate/up stage over the sorted buffer.
 
     Returns (h8 uint8 [P, I], h_scale float32 [P, I/128], h float32 [P, I], valid bool [P]);
@@ -57,7 +69,8 @@ def g1u1(a8, a_scale, w1, w1_scale, sorted_ids, sorted_expert_ids, num_valid, to
             continue
         e = int(sorted_expert_ids[blk])
         tok = np.asarray(sorted_ids)[rows] // topk
-        h[rows], _ = expert_ffn_h(a8[tok], a_scale[tok], w1[e], w1_scale[e])
+        h[rows], _ = expert_ffn_h(a8[tok], a_scale[tok], w1[e], w1_scale[e],
+                                  None if fc2_smooth_scale is None else fc2_smooth_scale[e])
     h8, hs = quant.quant_1x128(h)
     h8[~valid] = 0
     hs[~valid] = 0
@@ -86,7 +99,7 @@ def down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sorted_e
     return out
 
 
-def layer_tokens(a8, a_scale, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights):
+def layer_tokens(a8, a_scale, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, fc2_smooth_scale=None):
     """Token-major evaluation of the expert part of the layer for a set of token rows.
 
     a8 [R, H], a_scale [R, H/128], topk_ids / topk_weights [R, k] are the rows of
@@ -105,7 +118,8 @@ def layer_tokens(a8, a_scale, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights
     hss = np.zeros((R, k, I // 128), dtype=np.float32)
     for e in np.unique(topk_ids):
         ii, jj = np.nonzero(topk_ids == e)
-        h, _ = expert_ffn_h(a8[ii], a_scale[ii], w1[int(e)], w1_scale[int(e)])
+        h, _ = expert_ffn_h(a8[ii], a_scale[ii], w1[int(e)], w1_scale[int(e)],
+                            None if fc2_smooth_scale is None else fc2_smooth_scale[int(e)])
         h8, hs = quant.quant_1x128(h)
         y[ii, jj] = gemm.gemm_blockscale(h8, hs, w2[int(e)], w2_scale[int(e)])
         hh[ii, jj], h8s[ii, jj], hss[ii, jj] = h, h8, hs

@@ -82,9 +82,9 @@ def test_invalid_arguments_return_codes(lib):
     assert L.moe_sort(_p(), _p(), 4, 16, 4, 16, 24, _p(), _p(), _p(), _p(), _p(), 1 << 20, None) == -2
     # g1u1: capacity below the worst case -> EINVAL; I % 128 -> EUNSUPPORTED
     assert L.moe_fp8_blockscale_g1u1(_p(), _p(), 2, 1, _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16, 100,
-                                     _p(), _p(), None) == -1
+                                     _p(), _p(), None, None) == -1
     assert L.moe_fp8_blockscale_g1u1(_p(), _p(), 2, 1, _p(), _p(), _p(), _p(), _p(), 16, 256, 100, 16, 4, 16, 304,
-                                     _p(), _p(), None) == -2
+                                     _p(), _p(), None, None) == -2
     # down: workspace too small
     assert L.moe_down_combine(_p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16, 304, _p(),
                               256, _p(), 8, None) == -1
@@ -111,7 +111,7 @@ def test_zero_rows_are_noops_without_touching_memory(lib):
     assert L.grouped_topk(N, 0, 16, N, 0, 16, 4, 2, 4, 1, 2.5, N, N, 4, N) == 0
     assert L.moe_sort(N, N, 4, 0, 4, 16, 16, N, N, N, N, N, 0, N) == 0
     assert L.fp8_quant_1x128(N, 256, 0, 256, N, 256, N, 2, 1, N) == 0
-    assert L.moe_fp8_blockscale_g1u1(N, N, 2, 1, N, N, N, N, N, 0, 256, 128, 16, 4, 16, 256, N, N, N) == 0
+    assert L.moe_fp8_blockscale_g1u1(N, N, 2, 1, N, N, N, N, N, 0, 256, 128, 16, 4, 16, 256, N, N, N, N) == 0
     assert L.moe_down_combine(N, N, N, N, N, N, N, N, 0, 256, 128, 16, 4, 16, 256, N, 256, N, 0, N) == 0
     assert L.gemm_fp8_blockscale(N, N, 2, 1, N, N, 0, 256, 256, N, 256, 0, N, 0, N) == 0
     # ...but shape rules still apply

@@ -159,13 +159,19 @@ def _tiny_stage_inputs(tiny, BM):
 
 
 @pytest.mark.parametrize("BM", [16, 32, 64, 128])
-def test_g1u1_stage_tiny(m, tiny, BM):
+@pytest.mark.parametrize("smooth", [False, True], ids=["plain", "smooth"])
+def test_g1u1_stage_tiny(m, tiny, BM, smooth):
     cfg, x, w, ids, (sid, sw, seid, P), a8, sa = _tiny_stage_inputs(tiny, BM)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    sm = None
+    if smooth:  # per-expert channel factors spanning 2^-3 .. 2^3
+        sm = np.exp2(np.random.default_rng(BM).uniform(-3, 3, (cfg.E, cfg.I))).astype(np.float32)
     h8, hs = m.moe_fp8_blockscale_g1u1(t(a8), t(sa), x["w1"].to(DEV), x["w1_scale"].to(DEV), t(sid), t(seid),
-                                       t(np.array([P], np.int32)), cfg.topk, BM)
+                                       t(np.array([P], np.int32)), cfg.topk, BM,
+                                       fc2_smooth_scale=None if sm is None else t(sm))
     torch.cuda.synchronize()
-    _, _, h_ref, valid = oracle.moe.g1u1(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), sid, seid, P, cfg.topk, BM)
+    _, _, h_ref, valid = oracle.moe.g1u1(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), sid, seid, P, cfg.topk, BM,
+                                         fc2_smooth_scale=sm)
     rows = np.nonzero(valid)[0]
     check_requant(np_u8(h8)[rows], hs.cpu().numpy()[rows], h_ref[rows])
 

@@ -81,3 +81,38 @@ def test_topk1_identity_down_returns_dequantised_h(rng):
     out = moe.down_combine(h8, hs, w2, s2, sid, sw, seid, P, T, 1, 16)
     for r in np.nonzero(valid)[0]:
         assert np.array_equal(out[sid[r]], quant.dequant_1x128(h8[r:r + 1], hs[r:r + 1])[0])
+
+
+def test_smoothing_by_powers_of_two_moves_only_the_scales(rng):
+    # a factor 2^j on a whole 128-column group of h multiplies the group's amax, hence
+    # its 1x128 scale, by 2^j exactly, and leaves every e4m3 code unchanged
+    T, H, I, E = 6, 256, 256, 4
+    a8, sa, w1, s1, w2, s2, w, ids = _small_layer(rng, T=T, H=H, I=I, E=E, k=2)
+    sid, sw, seid, P = sort.moe_sort(ids, w, E, 16)
+    h8, hs, h, valid = moe.g1u1(a8, sa, w1, s1, sid, seid, P, 2, 16)
+    j = rng.integers(-3, 4, (E, I // 128))
+    smooth = np.repeat(np.ldexp(np.float32(1), j), 128, axis=1).astype(np.float32)
+    h8s, hss, hsm, _ = moe.g1u1(a8, sa, w1, s1, sid, seid, P, 2, 16, fc2_smooth_scale=smooth)
+    rows = np.nonzero(valid)[0]
+    e_of_row = np.asarray(seid)[rows // 16]
+    assert np.array_equal(h8s[rows], h8[rows])
+    assert np.array_equal(hss[rows], (hs[rows] * np.ldexp(np.float32(1), j[e_of_row])).astype(np.float32))
+    # all-ones factors are the unsmoothed layer
+    h81, hs1, _, _ = moe.g1u1(a8, sa, w1, s1, sid, seid, P, 2, 16, fc2_smooth_scale=np.ones((E, I), np.float32))
+    assert np.array_equal(h81, h8) and np.array_equal(hs1, hs)
+
+
+def test_smoothing_zero_channel_zeroes_its_codes(rng):
+    # a zero factor silences exactly its channel: code 0 there, the other channels keep
+    # their values up to the group's re-derived scale
+    T, H, I, E = 5, 128, 128, 2
+    a8, sa, w1, s1, w2, s2, w, ids = _small_layer(rng, T=T, H=H, I=I, E=E, k=1)
+    sid, sw, seid, P = sort.moe_sort(ids, w, E, 16)
+    smooth = np.ones((E, I), np.float32)
+    smooth[:, 7] = 0.0
+    h8, hs, h, valid = moe.g1u1(a8, sa, w1, s1, sid, seid, P, 1, 16, fc2_smooth_scale=smooth)
+    rows = np.nonzero(valid)[0]
+    assert np.all(h8[rows, 7] & 0x7F == 0)
+    _, _, hraw, _ = moe.g1u1(a8, sa, w1, s1, sid, seid, P, 1, 16)
+    keep = np.arange(I) != 7
+    assert np.array_equal(h[np.ix_(rows, keep)], hraw[np.ix_(rows, keep)])
