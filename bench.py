@@ -195,6 +195,33 @@ def bench_moe(a):
     ms = start.elapsed_time(end) / a.steps
     g1u1_ms = sum(s.elapsed_time(e) for s, e in ev) / a.steps
 
+    # per-call breakdown (outside the timed region): events around each of the five calls
+    calls = [
+        ("grouped_topk", lambda: m.grouped_topk(logits, layer.bias, c.n_group, c.topk_group, c.topk, c.renorm,
+                                                c.routed_scaling_factor, layer.topk_w, layer.topk_ids)),
+        ("moe_sort", lambda: m.moe_sort(layer.topk_ids, layer.topk_w, c.E, bm, layer.sort_out, layer.sort_ws)),
+        ("fp8_quant_1x128", lambda: m.fp8_quant_1x128(hidden, layer.a8, layer.a_scale)),
+        ("moe_fp8_blockscale_g1u1", lambda: m.moe_fp8_blockscale_g1u1(layer.a8, layer.a_scale, layer.w1,
+                                                                      layer.w1_scale, sid, seid, nv, c.topk, bm,
+                                                                      layer.h8, layer.h_scale)),
+        ("moe_down_combine", lambda: m.moe_down_combine(layer.h8, layer.h_scale, layer.w2, layer.w2_scale, sid, sw,
+                                                        seid, nv, layer.T, c.topk, bm, layer.out,
+                                                        layer.down_ws)),
+    ]
+    reps = max(10, a.steps)
+    cev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+           for _ in range(reps)]
+    for r in range(reps):
+        for (name, fn), (e0, e1) in zip(calls, cev[r]):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    per_call = {}
+    for ci, (name, _) in enumerate(calls):
+        t = sorted(cev[r][ci][0].elapsed_time(cev[r][ci][1]) for r in range(reps))
+        per_call[name] = {"median_ms": t[len(t) // 2], "min_ms": t[0]}
+
     ids = layer.topk_ids.cpu().numpy()
     hot = inputs.hot_expert_mask(cfg, dev, a.seed).cpu().numpy() if cfg.skew else None
     rs = routing_stats(ids, cfg.E, bm, hot)
@@ -231,7 +258,7 @@ def bench_moe(a):
         "layer_tflops": flops / (ms * 1e-3) / 1e12, "layer_gbs": nbytes / (ms * 1e-3) / 1e9,
         "layer_frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
-        "routing": rs, "roofline": roof, "input_gen_s": round(gen_s, 2),
+        "routing": rs, "roofline": roof, "per_call_ms": per_call, "input_gen_s": round(gen_s, 2),
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_moe(cfg, hidden, logits, layer.bias, layer.w1, layer.w1_scale, layer.w2,

@@ -18,14 +18,17 @@
 // DMAs with s_waitcnt vmcnt and a bare s_barrier publishes the stage.
 //
 // Modes:
-//   dense  C[M, N] = A[M, K] B[N, K]^T, bf16 out ("General Linear Layer").
+//   dense  C[M, N] = A[M, K] B[N, K]^T, bf16 or fp16 out ("General Linear
+//          Layer"); small M splits K over workgroups into fp32 partials that
+//          a reduce kernel adds in a fixed order.
 //   g1u1   grouped GEMM over the sorted token-expert pairs ("Complete MoE
 //          Implementation" / "Blockscale FP8 MoE Computation"): A rows
 //          gathered through sorted_ids, B = 128 gate rows and the matching 128
-//          up rows of the block's expert; epilogue h = SiLU(gate) * up and a
-//          1x128 e4m3 requantisation of h.
+//          up rows of the block's expert; epilogue h = SiLU(gate) * up
+//          (optionally times per-channel smoothing factors) and a 1x128 e4m3
+//          requantisation of h.
 //   down   grouped GEMM of h with the expert's down weights; each row is
-//          scaled by its routing weight and staged per flat pair; a second
+//          scaled by its routing weight and stored per flat pair; a second
 //          kernel sums each token's pairs in ascending order into bf16.
 #include <algorithm>
 #include <type_traits>
