@@ -11,6 +11,8 @@ Reading taken for the steps the page leaves open, per group x[0..127]:
   q_i   = encode(fl32(x_i / scale))           (IEEE fp32 division, RNE,
                                                saturating, sign kept)
 The scale is a dequantisation multiplier: value = decode(q) * scale.
+When K is not a multiple of 128 the last group of a row holds the remaining
+K mod 128 values (ceil(K/128) scales per row, as the pages size them).
 """
 import numpy as np
 
@@ -20,16 +22,19 @@ GROUP = 128
 
 
 def quant_1x128(x):
-    """x: float32 [M, K], K % 128 == 0 -> (q uint8 [M, K], scale float32 [M, K/128])."""
+    """x: float32 [M, K] -> (q uint8 [M, K], scale float32 [M, ceil(K/128)])."""
     x = np.asarray(x, dtype=np.float32)
     M, K = x.shape
-    assert K % GROUP == 0
-    g = x.reshape(M, K // GROUP, GROUP)
-    amax = np.max(np.abs(g), axis=2)                                     # float32, exact
-    scale = np.divide(amax, np.float32(fp8.E4M3_MAX), dtype=np.float32)  # fl32(amax/448)
-    scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
-    y = np.divide(g, scale[:, :, None], dtype=np.float32)               # fl32(x/scale)
-    q = fp8.encode(y).reshape(M, K)
+    KB = -(-K // GROUP)
+    q = np.zeros((M, K), dtype=np.uint8)
+    scale = np.ones((M, KB), dtype=np.float32)
+    for kb in range(KB):
+        g = x[:, kb * GROUP:(kb + 1) * GROUP]                               # the last may be shorter
+        amax = np.max(np.abs(g), axis=1)                                     # float32, exact
+        s = np.divide(amax, np.float32(fp8.E4M3_MAX), dtype=np.float32)    # fl32(amax/448)
+        s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+        q[:, kb * GROUP:(kb + 1) * GROUP] = fp8.encode(np.divide(g, s[:, None], dtype=np.float32))
+        scale[:, kb] = s
     return q, scale
 
 
@@ -37,5 +42,5 @@ def dequant_1x128(q, scale):
     """decode(q) * scale per 1x128 group, binary64."""
     q = np.asarray(q, dtype=np.uint8)
     M, K = q.shape
-    v = fp8.decode(q).reshape(M, K // GROUP, GROUP)
-    return (v * np.asarray(scale, dtype=np.float64)[:, :, None]).reshape(M, K)
+    s = np.repeat(np.asarray(scale, dtype=np.float64), GROUP, axis=1)[:, :K]
+    return fp8.decode(q) * s

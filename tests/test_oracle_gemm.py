@@ -41,3 +41,37 @@ def test_against_dequantised_torch_matmul(rng):
     B = torch.from_numpy(fp8.decode(b) * np.repeat(np.repeat(sb.astype(np.float64), 128, 0), 128, 1))
     ref = (A @ B.T).numpy()
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_partial_blocks_brute_force(rng):
+    # K and N not multiples of 128: element-by-element sum with the scale of each k's block
+    M, N, K = 3, 136, 144
+    a = _codes(rng, (M, K)) & 0xF7
+    b = _codes(rng, (N, K)) & 0xF7
+    sa = (rng.random((M, 2)) + 0.5).astype(np.float32)
+    sb = (rng.random((2, 2)) + 0.5).astype(np.float32)
+    out = gemm.gemm_blockscale(a, sa, b, sb)
+    A, B = fp8.decode(a).tolist(), fp8.decode(b).tolist()
+    sal, sbl = sa.astype(np.float64).tolist(), sb.astype(np.float64).tolist()
+    for m in range(M):
+        for n in range(N):
+            ref = sum(sal[m][k // 128] * sbl[n // 128][k // 128] * A[m][k] * B[n][k] for k in range(K))
+            assert abs(out[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_partial_blocks_equal_zero_padded_problem(rng):
+    # zero codes appended along K (and rows along N) change no block sum: the padded
+    # problem's leading N columns reproduce the partial one bit for bit
+    M, N, K = 5, 200, 328
+    a = _codes(rng, (M, K)) & 0xF7
+    b = _codes(rng, (N, K)) & 0xF7
+    sa = (rng.random((M, 3)) + 0.5).astype(np.float32)
+    sb = (rng.random((2, 3)) + 0.5).astype(np.float32)
+    out = gemm.gemm_blockscale(a, sa, b, sb)
+    ap = np.zeros((M, 384), np.uint8)
+    ap[:, :K] = a
+    bp = np.zeros((256, 384), np.uint8)
+    bp[:N, :K] = b
+    full = gemm.gemm_blockscale(ap, sa, bp, sb)
+    assert np.array_equal(out, full[:, :N])
+    assert np.array_equal(gemm.block_sums(a, b), gemm.block_sums(ap, bp)[:, :, :N])

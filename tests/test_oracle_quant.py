@@ -51,3 +51,22 @@ def test_amax_maps_to_448_and_error_bound(rng):
     deq = quant.dequant_1x128(q, s).reshape(32, 4, 128)
     bound = np.abs(g) * 2.0 ** -4 + s[..., None].astype(np.float64) * 2.0 ** -10 + 1e-12
     assert np.all(np.abs(deq - g) <= bound * (1 + 1e-6))
+
+
+def test_partial_last_group_matches_torch(rng):
+    # K = 200: groups of 128 and 72 values, each with its own amax
+    x = (rng.standard_normal((16, 200)) * np.exp2(rng.integers(-8, 8, (16, 1)))).astype(np.float32)
+    x[3, 128:] = 0.0                                   # an all-zero tail group keeps scale 1
+    q, s = quant.quant_1x128(x)
+    assert q.shape == (16, 200) and s.shape == (16, 2)
+    xt = torch.from_numpy(x)
+    for kb, (lo, hi) in enumerate(((0, 128), (128, 200))):
+        g = xt[:, lo:hi]
+        amax = g.abs().amax(-1)
+        st = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)
+        qt = (g / st[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        assert np.array_equal(s[:, kb], st.numpy())
+        assert np.array_equal(q[:, lo:hi], qt.numpy())
+    assert s[3, 1] == 1.0 and np.all(q[3, 128:] == 0)
+    deq = quant.dequant_1x128(q, s)
+    assert np.all(np.abs(deq - x) <= np.abs(x) * 2.0 ** -4 + np.repeat(s, 128, 1)[:, :200] * 2.0 ** -10 + 1e-12)
