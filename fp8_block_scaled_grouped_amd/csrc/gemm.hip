@@ -146,6 +146,12 @@ __device__ __forceinline__ void vm_wait_stages(int a) {
   }
 }
 
+__device__ __forceinline__ void lgkm_wait0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0), vmcnt and expcnt untouched
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -163,8 +169,13 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r0, int lane) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <class C, int MODE>
+// PK (dense only): K is not a multiple of 128, so the last K block holds
+// K % 128 bytes of each row.  Its chunks past K are fetched from the row's
+// first chunk (in bounds) and overwritten with zeros in LDS once the stage has
+// landed, so they add nothing to the block sum.
+template <class C, int MODE, bool PK = false>
 __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
+  static_assert(!PK || MODE == kDense, "partial K blocks: dense mode only");
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLds];
   __shared__ int rowinfo[C::BM];
   __shared__ float red[C::kRed][C::BM];
@@ -172,8 +183,10 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in SGPRs
   const int wm = w / C::kWN, wn = w % C::kWN;
-  const int NT = g.N / C::kOutN;
-  const int KBtot = g.K / 128;  // K blocks of the whole problem (row stride of the B scales)
+  // dense N may end inside a tile: the last tile's B rows past N repeat row N-1
+  // and its columns past N are not stored
+  const int NT = MODE == kDense ? (g.N + C::kOutN - 1) / C::kOutN : g.N / C::kOutN;
+  const int KBtot = (g.K + 127) / 128;  // K blocks of the whole problem (row stride of the B scales)
   const int npairs = g.T * g.topk;
 
   // Tiles are (M block, N tile) pairs, N tile fastest, one per workgroup: the N
@@ -200,6 +213,9 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   if (tile >= total) return;  // uniform: blocks past num_valid hold no rows
   const int kbase = ks * g.kbs;                        // first K block of this split
   const int KB = min(g.kbs, KBtot - kbase);            // K blocks this workgroup walks
+  // blocks the DMA pipeline walks: with PK the last, partial block of K (if this
+  // workgroup owns it) is staged separately after the pipeline
+  const int KBp = PK && kbase + KB == KBtot ? KB - 1 : KB;
   const int nt = (int)(tile % NT);
   const int mb = (int)(tile / NT);
   const int64_t row0 = (int64_t)mb * C::BM;
@@ -213,7 +229,8 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   const int colofs = (wn % (C::kWN / C::kParts)) * C::kWTNB;  // first output column of this wave in its part
   const float* sbp;
   if constexpr (MODE == kDense) {
-    sbp = g.b_scale + (int64_t)((nt * C::BNB + wn * C::kWTNB) / 128) * KBtot + kbase;
+    const int nb = min((nt * C::BNB + wn * C::kWTNB) / 128, (g.N + 127) / 128 - 1);  // waves past N: any valid row
+    sbp = g.b_scale + (int64_t)nb * KBtot + kbase;
   } else if constexpr (MODE == kG1U1) {
     const int64_t nb2 = 2 * (g.N / 128);
     sbp = g.b_scale + ((int64_t)expert * nb2 + (part == 0 ? nt : g.N / 128 + nt)) * KBtot;
@@ -251,6 +268,8 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   auto b_row = [&](int r) -> int {
     if constexpr (MODE == kG1U1) {
       return r < 128 ? nt * 128 + r : g.N + nt * 128 + (r - 128);
+    } else if constexpr (MODE == kDense) {
+      return min(nt * C::BNB + r, g.N - 1);
     } else {
       return nt * C::BNB + r;
     }
@@ -316,7 +335,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
   for (int s = 0; s < C::S - 1; ++s)
-    if (s < KB) issue(s, s);
+    if (s < KBp) issue(s, s);
 
   // one K step on LDS stage `stage`; only the first TMV row tiles of the wave are computed
   // RF 1: the step refills its stage (steady state, no branches); RF 0: checked
@@ -326,10 +345,10 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     if constexpr (RF == 1) {
       vm_wait<(C::S - 2) * C::kLoadsPerStage>();
     } else {
-      vm_wait_stages<C::kLoadsPerStage>(min(C::S - 2, KB - 1 - kb));
+      vm_wait_stages<C::kLoadsPerStage>(min(C::S - 2, KBp - 1 - kb));
     }
     barrier_only();
-    const bool refill = RF == 1 || kb + C::S - 1 < KB;
+    const bool refill = RF == 1 || kb + C::S - 1 < KBp;
     const int nstage = (stage + C::S - 1) % C::S, nkb = kb + C::S - 1;
     if constexpr (TMV == 0) {
       if (refill) issue(nstage, nkb);
@@ -368,15 +387,37 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   // unrolled by the stage count: every LDS address is base + immediate
   auto kloop = [&](auto tmv_c) {
     int kb0 = 0;
-    // rounds whose every step refills (kb + S - 1 < KB for the round's last step)
-    for (; kb0 + 2 * C::S - 1 <= KB; kb0 += C::S) {
+    // rounds whose every step refills (kb + S - 1 < KBp for the round's last step)
+    for (; kb0 + 2 * C::S - 1 <= KBp; kb0 += C::S) {
 #pragma unroll
       for (int u = 0; u < C::S; ++u) step(kb0 + u, u, tmv_c, std::integral_constant<int, 1>{});
     }
-    for (; kb0 < KB; kb0 += C::S) {
+    for (; kb0 < KBp; kb0 += C::S) {
 #pragma unroll
       for (int u = 0; u < C::S; ++u)
-        if (kb0 + u < KB) step(kb0 + u, u, tmv_c, std::integral_constant<int, 0>{});
+        if (kb0 + u < KBp) step(kb0 + u, u, tmv_c, std::integral_constant<int, 0>{});
+    }
+    if constexpr (PK) {
+      if (KBp < KB) {
+        // the last, partial K block goes through registers into stage 0, chunks
+        // past K as zeros (they then add nothing to the block sum)
+        __syncthreads();  // every wave is done with the pipeline's stages
+        const int64_t kg = KBtot - 1;
+        const int kt = g.K - (int)kg * 128;  // bytes of each row inside K
+        // this lane's chunk inside its row (rows of a 1 KB DMA block start at multiples of 8)
+        const int chb = ((lane & 7) ^ ((lane >> 3) & 7)) * 16;
+#pragma unroll
+        for (int j = 0; j < C::kQW; ++j) {
+          const int q = w + j * C::NW;
+          u32x4 v{0u, 0u, 0u, 0u};
+          if (chb < kt) v = *reinterpret_cast<const u32x4*>((q < C::kAQ ? a_base : b_base) + kg * 128 + voff[j]);
+          *reinterpret_cast<u32x4*>(lds + q * 1024 + lane * 16) = v;
+        }
+        *reinterpret_cast<float*>(lds + sofs + lane * 4) =
+            *reinterpret_cast<const float*>(s_base + kg * g.sskb * 4 + soff);
+        lgkm_wait0();
+        step(KBp, 0, tmv_c, std::integral_constant<int, 0>{});
+      }
     }
   };
   static_assert(C::kTM <= 4, "row tiles per wave");
@@ -410,7 +451,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     for (int ci = tid; ci < C::BM * CPR; ci += C::kThreads) {
       const int r = ci / CPR, ch = ci % CPR;
       const int64_t m = row0 + r;
-      if (m < g.M)
+      if (m < g.M && nt * C::BNB + ch * 4 < g.N)  // N % 8 == 0: a chunk is all in or all out
         *reinterpret_cast<u32x4*>(dst + m * g.N + (int64_t)nt * C::BNB + ch * 4) =
             *reinterpret_cast<const u32x4*>(ob + r * RS + ch * 4);
     }
@@ -431,7 +472,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     for (int ci = tid; ci < C::BM * CPR; ci += C::kThreads) {
       const int r = ci / CPR, ch = ci % CPR;
       const int64_t m = row0 + r;
-      if (m < g.M)
+      if (m < g.M && nt * C::BNB + ch * 8 < g.N)
         *reinterpret_cast<u32x4*>(g.c + m * g.ldc + (int64_t)nt * C::BNB + ch * 8) =
             *reinterpret_cast<const u32x4*>(ob + r * RS + ch * 8);
     }
@@ -582,25 +623,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-template <class C, int MODE>
+template <class C, int MODE, bool PK>
 int launch_cfg(const GemmArgs& g, int64_t mblocks, hipStream_t stream) {
-  if (g.N % C::kOutN != 0) return MOE355_EUNSUPPORTED;
-  const int64_t grid = mblocks * (g.N / C::kOutN) * (MODE == kDense ? g.splits : 1);
+  if (MODE != kDense && g.N % C::kOutN != 0) return MOE355_EUNSUPPORTED;
+  const int64_t grid = mblocks * ceil_div64(g.N, C::kOutN) * (MODE == kDense ? g.splits : 1);
   if (grid == 0) return MOE355_OK;
   MOE355_CHECK(grid < (1ll << 31), MOE355_EUNSUPPORTED);
-  hipLaunchKernelGGL((bs_gemm_kernel<C, MODE>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, g);
+  hipLaunchKernelGGL((bs_gemm_kernel<C, MODE, PK>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, g);
   return launch_status();
 }
 
 // Tile choice per M tile: small tiles stream weights (decode, small M), 128-row
 // tiles with 8 waves feed the matrix cores (prefill, large M).
-template <int MODE, int BNB = 256>
+template <int MODE, int BNB = 256, bool PK = false>
 int launch_gemm(const GemmArgs& g, int bm, int64_t mblocks, hipStream_t stream) {
   switch (bm) {
-    case 16: return launch_cfg<Cfg<MODE, 16, BNB, 4, 1, 4>, MODE>(g, mblocks, stream);
-    case 32: return launch_cfg<Cfg<MODE, 32, BNB, 4, 1, 4>, MODE>(g, mblocks, stream);
-    case 64: return launch_cfg<Cfg<MODE, 64, BNB, 4, 1, 3>, MODE>(g, mblocks, stream);
-    case 128: return launch_cfg<Cfg<MODE, 128, BNB, 8, 2, 3>, MODE>(g, mblocks, stream);
+    case 16: return launch_cfg<Cfg<MODE, 16, BNB, 4, 1, 4>, MODE, PK>(g, mblocks, stream);
+    case 32: return launch_cfg<Cfg<MODE, 32, BNB, 4, 1, 4>, MODE, PK>(g, mblocks, stream);
+    case 64: return launch_cfg<Cfg<MODE, 64, BNB, 4, 1, 3>, MODE, PK>(g, mblocks, stream);
+    case 128: return launch_cfg<Cfg<MODE, 128, BNB, 8, 2, 3>, MODE, PK>(g, mblocks, stream);
     default: return MOE355_EUNSUPPORTED;
   }
 }
@@ -624,8 +665,8 @@ DensePlan dense_plan(int M, int N, int K) {
   DensePlan p;
   p.bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
   p.bnb = (N % 256 != 0 || (M <= 64 && N <= kNarrowMaxN)) ? 128 : 256;
-  const int KB = K / 128;
-  const int64_t base = ceil_div64(M, p.bm) * (N / p.bnb);
+  const int KB = (int)ceil_div64(K, 128);
+  const int64_t base = ceil_div64(M, p.bm) * ceil_div64(N, p.bnb);
   int splits = 1;
   if (M <= 64 && 2 * base <= kSplitTargetWG && KB >= 4) {
     const int64_t by_bytes = std::max<int64_t>(1, K / (kSplitBytesDiv * 4 * M));
@@ -654,7 +695,7 @@ using namespace moe355;
 
 extern "C" int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes) {
   MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && bytes, MOE355_EINVAL);
-  MOE355_CHECK(K % 128 == 0 && N % 128 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
+  MOE355_CHECK(K % 16 == 0 && N % 8 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
   *bytes = (M == 0 || N == 0 || K == 0) ? 0 : dense_workspace_bytes(dense_plan(M, N, K), M, N);
   return MOE355_OK;
 }
@@ -664,7 +705,7 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
                                    int64_t ldc, int out_fp16, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream) {
   MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && ldc >= N && (out_fp16 == 0 || out_fp16 == 1), MOE355_EINVAL);
-  MOE355_CHECK(K % 128 == 0 && N % 128 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
+  MOE355_CHECK(K % 16 == 0 && N % 8 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
   MOE355_CHECK((int64_t)M * K < (1ll << 32) && (int64_t)N * K < (1ll << 32), MOE355_EUNSUPPORTED);
   if (M == 0 || N == 0) return MOE355_OK;
   MOE355_CHECK(K > 0 && a8 && a_scale && b8 && b_scale && c && sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
@@ -675,7 +716,7 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
   if (need == 0 || workspace == nullptr || workspace_bytes < need) {
     // without (enough) workspace: one workgroup per output tile walks all of K
     plan.splits = 1;
-    plan.kbs = K / 128;
+    plan.kbs = (int)ceil_div64(K, 128);
   } else {
     MOE355_CHECK(aligned16(workspace), MOE355_EMISALIGNED);
   }
@@ -696,8 +737,14 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
   g.out_f16 = out_fp16;
   g.part = static_cast<float*>(workspace);
   const int64_t mblocks = ceil_div64(M, plan.bm);
-  const int st = plan.bnb == 128 ? launch_gemm<kDense, 128>(g, plan.bm, mblocks, stream)
-                                 : launch_gemm<kDense, 256>(g, plan.bm, mblocks, stream);
+  int st;
+  if (K % 128 == 0) {
+    st = plan.bnb == 128 ? launch_gemm<kDense, 128>(g, plan.bm, mblocks, stream)
+                         : launch_gemm<kDense, 256>(g, plan.bm, mblocks, stream);
+  } else {
+    st = plan.bnb == 128 ? launch_gemm<kDense, 128, true>(g, plan.bm, mblocks, stream)
+                         : launch_gemm<kDense, 256, true>(g, plan.bm, mblocks, stream);
+  }
   if (st != MOE355_OK || plan.splits == 1) return st;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)ceil_div64(N, 256), (unsigned)M), dim3(256), 0, stream,
                      g.part, plan.splits, M, N, c, ldc, out_fp16);

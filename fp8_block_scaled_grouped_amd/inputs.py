@@ -76,16 +76,21 @@ def bf16_bits(x):
 
 
 def quantize_weight_blocks(w):
-    """fp32 [..., R, C] -> (e4m3 bytes uint8 [..., R, C], fp32 scales [..., R/128, C/128]).
+    """fp32 [..., R, C] -> (e4m3 bytes uint8 [..., R, C], fp32 scales [..., ceil(R/128), ceil(C/128)]).
 
-    Checkpoint-style weight preparation with torch's cast (saturated to +-448).
+    Checkpoint-style weight preparation with torch's cast (saturated to +-448);
+    a last, shorter block takes the amax of the values it holds.
     """
     *lead, R, C = w.shape
-    blk = w.reshape(*lead, R // 128, 128, C // 128, 128)
+    Rp, Cp = -(-R // 128) * 128, -(-C // 128) * 128
+    if (Rp, Cp) != (R, C):
+        w = torch.nn.functional.pad(w, (0, Cp - C, 0, Rp - R))       # zeros leave each amax as it is
+    blk = w.reshape(*lead, Rp // 128, 128, Cp // 128, 128)
     amax = blk.abs().amax(dim=(-3, -1))
     scale = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)
     q = (blk / scale[..., :, None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
-    return q.reshape(*lead, R, C).view(torch.uint8), scale.float().contiguous()
+    q = q.reshape(*lead, Rp, Cp)[..., :R, :C].contiguous()
+    return q.view(torch.uint8), scale.float().contiguous()
 
 
 def _expert_weights(E, R, C, device, seed, stream, std=0.02):
@@ -147,15 +152,15 @@ def make_moe_inputs(cfg, device="cpu", seed=0, weights=True):
 
 
 def make_dense_inputs(M, N, K=DENSE_K, device="cpu", seed=0):
-    """A bf16 [M, K] ~N(0,1); B e4m3 [N, K] with fp32 [N/128, K/128] scales, from N(0,0.02)."""
+    """A bf16 [M, K] ~N(0,1); B e4m3 [N, K] with fp32 [ceil(N/128), ceil(K/128)] scales, from N(0,0.02)."""
     a = torch.randn((M, K), generator=_gen(device, seed, _S_DA), device=device).to(torch.bfloat16)
     g = _gen(device, seed, _S_DB)
     b = torch.empty((N, K), dtype=torch.uint8, device=device)
-    bs = torch.empty((N // 128, K // 128), dtype=torch.float32, device=device)
+    bs = torch.empty((ceil_div(N, 128), ceil_div(K, 128)), dtype=torch.float32, device=device)
     step = 2048
     for n0 in range(0, N, step):
         w = torch.randn((min(step, N - n0), K), generator=g, device=device) * 0.02
-        b[n0:n0 + w.shape[0]], bs[n0 // 128:(n0 + w.shape[0]) // 128] = quantize_weight_blocks(w)
+        b[n0:n0 + w.shape[0]], bs[n0 // 128:ceil_div(n0 + w.shape[0], 128)] = quantize_weight_blocks(w)
     return {"a": a.contiguous(), "b": b, "b_scale": bs}
 
 

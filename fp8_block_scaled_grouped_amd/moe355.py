@@ -155,26 +155,33 @@ def moe_sort(topk_ids, topk_weights, E, block_m, out=None, workspace=None):
 def fp8_quant_1x128(x, q=None, scale=None, scale_layout="row"):
     """bf16 [M, K] -> (e4m3 uint8 [M, K], fp32 scales).
 
-    scale_layout "row": scales [M, K/128]; "kblock": scales [K/128, M].
+    scale_layout "row": scales [M, KB]; "kblock": scales [KB, M]; KB = ceil(K/128).
     """
     _dev(x, torch.bfloat16, "x")
     M, K = x.shape
+    KB = _nblk(K)
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if scale is None:
-        shape = (M, K // 128) if scale_layout == "row" else (K // 128, M)
+        shape = (M, KB) if scale_layout == "row" else (KB, M)
         scale = torch.empty(shape, dtype=torch.float32, device=x.device)
-    ssm, sskb = (K // 128, 1) if scale_layout == "row" else (1, M)
+    ssm, sskb = (KB, 1) if scale_layout == "row" else (1, M)
     _check(lib().fp8_quant_1x128(_ptr(x), _rows(x, "x"), M, K, _ptr(q), _rows(q, "q"), _ptr(scale), ssm, sskb,
                                  _stream()))
     return q, scale
 
 
+def _nblk(n):
+    """ceil(n / 128): scale entries along a dimension of n."""
+    return -(-n // 128)
+
+
 def _scale_strides(a_scale, T, H, scale_layout):
+    KB = _nblk(H)
     if scale_layout == "row":
-        assert a_scale.shape == (T, H // 128)
-        return H // 128, 1
-    assert a_scale.shape == (H // 128, T)
+        assert a_scale.shape == (T, KB)
+        return KB, 1
+    assert a_scale.shape == (KB, T)
     return 1, T
 
 
@@ -239,7 +246,8 @@ def gemm_fp8_blockscale_workspace(M, N, K):
 def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row", workspace=None,
                         out_dtype=torch.bfloat16):
     """a8 e4m3 [M, K] (1x128 scales), b8 e4m3 [N, K] (128x128 scales) -> [M, N] in out_dtype
-    (bf16 or fp16; taken from c when c is given).
+    (bf16 or fp16; taken from c when c is given).  K and N need not be multiples of
+    128: a_scale [M, ceil(K/128)], b_scale [ceil(N/128), ceil(K/128)].
 
     workspace: None allocates what gemm_fp8_blockscale_workspace asks for; False runs
     without workspace (no split-K); or a device uint8 tensor.
@@ -248,6 +256,10 @@ def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row", wo
     _dev(b8, torch.uint8, "b8")
     M, K = a8.shape
     N = b8.shape[0]
+    if b8.shape[1] != K or b_scale.shape != (_nblk(N), _nblk(K)):
+        raise ValueError("b8 [N, K] with b_scale [ceil(N/128), ceil(K/128)] expected")
+    if not _dev(b_scale, torch.float32, "b_scale").is_contiguous():
+        raise ValueError("b_scale must be contiguous")
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype, device=a8.device)
     if c.dtype not in (torch.bfloat16, torch.float16):

@@ -118,14 +118,16 @@ int moe_sort(const int32_t* topk_ids, const float* topk_weights, int64_t ld_topk
  * Dynamic 1x128 FP8 quantisation ("General Linear Layer": one scale per 1x128
  * of an activation row; "Blockscale FP8 MoE Computation": the bf16 hidden
  * states are quantised per 128 before the grouped GEMM).  Per row m and
- * group kb (columns [128*kb, 128*kb+128)):
+ * group kb (columns [128*kb, min(K, 128*kb+128)); the last group of a row holds
+ * the remaining K % 128 values when K is not a multiple of 128):
  *   amax  = max |x|;  scale = (amax == 0) ? 1 : fl32(amax / 448)
  *   q     = e4m3(fl32(x / scale))  nearest-even, saturating at +-448, sign kept
  * x      bf16 bits [M, K], row stride ld_x >= K.
  * q      e4m3 [M, K] out, row stride ld_q >= K.
  * scale  fp32 out, element (m, kb) at scale[m*sstride_m + kb*sstride_kb]:
- *        row-major [M, K/128] is (K/128, 1); K-block-major [K/128, M] is (1, M).
- * K % 128 == 0.  x, q and their row strides (in bytes) must be 16-byte aligned.
+ *        row-major [M, KB] is (KB, 1); K-block-major [KB, M] is (1, M); KB = ceil(K/128).
+ * K % 8 == 0 (else MOE355_EUNSUPPORTED).  x and q 16-byte aligned, x's row stride a
+ * multiple of 16 bytes and q's of 8 (each lane stores 8 codes), else MOE355_EMISALIGNED.
  */
 int fp8_quant_1x128(const uint16_t* x, int64_t ld_x, int M, int K,
                     uint8_t* q, int64_t ld_q,
@@ -198,7 +200,10 @@ int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes);
  * times (WQ, 128x128 scales)^T with WQ stored [N, K]):
  *   c[m,n] = bf16( sum_kb a_scale(m,kb) * b_scale[n/128, kb] * sum_{k in kb} a8[m,k] * b8[n,k] )
  * a8       e4m3 [M, K] (row stride K); a_scale(m,kb) = a_scale[m*sstride_m + kb*sstride_kb].
- * b8       e4m3 [N, K] (row stride K); b_scale fp32 [N/128, K/128].
+ * b8       e4m3 [N, K] (row stride K); b_scale fp32 [ceil(N/128), ceil(K/128)].
+ *          K and N need not be multiples of 128 (the section sizes its scale arrays
+ *          with ceil): K block kb covers k in [128*kb, min(K, 128*kb+128)) and
+ *          b_scale row n/128 serves the last, shorter column block.
  * c        [M, N] out, row stride ldc >= N (16-byte aligned rows): bf16 bits, or fp16
  *          bits when out_fp16 is 1 (the pages' linear layer offers both output types);
  *          round to nearest even either way.
@@ -206,7 +211,7 @@ int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes);
  *          then splits K over more workgroups, keeps fp32 partial sums there and adds them
  *          in a fixed order (deterministic); without it one workgroup per output
  *          tile walks all of K.  Contents need no initialisation.
- * K % 128 == 0, N % 128 == 0, K <= 16384; a8, b8 16-byte aligned.
+ * K % 16 == 0, N % 8 == 0, K <= 16384 (else MOE355_EUNSUPPORTED); a8, b8 16-byte aligned.
  */
 int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale,
                         int64_t sstride_m, int64_t sstride_kb,

@@ -67,12 +67,15 @@ def test_invalid_arguments_return_codes(lib):
     assert L.grouped_topk(None, 0, 16, _p(), 4, 16, 4, 2, 4, 1, 1.0, _p(), _p(), 4, None) == -1
     assert L.grouped_topk(_p(), 0, 16, _p(), 4, 16, 4, 2, 9, 1, 1.0, _p(), _p(), 9, None) == -2   # topk > tg*E/G
     assert L.grouped_topk(_p(), 0, 16, _p(), 0, 16, 4, 2, 4, 1, 1.0, None, None, 4, None) == 0    # T = 0 no-op
-    # quant: K % 128 -> EUNSUPPORTED; misaligned -> EMISALIGNED; ld < K -> EINVAL
-    assert L.fp8_quant_1x128(_p(), 200, 4, 200, _p(), 200, _p(), 2, 1, None) == -2
+    # quant: K % 8 -> EUNSUPPORTED; misaligned -> EMISALIGNED; ld < K -> EINVAL
+    assert L.fp8_quant_1x128(_p(), 204, 4, 204, _p(), 208, _p(), 2, 1, None) == -2
     assert L.fp8_quant_1x128(_p(8), 256, 4, 256, _p(), 256, _p(), 2, 1, None) == -3
+    assert L.fp8_quant_1x128(_p(), 256, 4, 256, _p(), 260, _p(), 2, 1, None) == -3
     assert L.fp8_quant_1x128(_p(), 128, 4, 256, _p(), 256, _p(), 2, 1, None) == -1
-    # dense GEMM: N % 128 -> EUNSUPPORTED; ldc < N -> EINVAL
-    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 100, 256, _p(), 100, 0, None, 0, None) == -2
+    # dense GEMM: N % 8 or K % 16 -> EUNSUPPORTED; ldc < N -> EINVAL
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 100, 256, _p(), 104, 0, None, 0, None) == -2
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 200, _p(), 128, 0, None, 0, None) == -2
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 120, 0, None, 0, None) == -1
     assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 64, 0, None, 0, None) == -1
     # output type flag must be 0 or 1; logits type flag likewise
     assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 128, 2, None, 0, None) == -1
@@ -100,8 +103,12 @@ def test_dense_workspace_query(lib):
     assert moe355.gemm_fp8_blockscale_workspace(4096, 18432, 7168) == 0
     assert moe355.gemm_fp8_blockscale_workspace(0, 2048, 7168) == 0
     assert moe355.gemm_fp8_blockscale_workspace(1, 2048, 256) == 0  # two K blocks: nothing to split
+    # partial blocks: K and N in ceil(./128) blocks
+    assert moe355.gemm_fp8_blockscale_workspace(1, 1000, 4112) > 0
     with pytest.raises(moe355.Moe355Error):
         moe355.gemm_fp8_blockscale_workspace(1, 100, 256)
+    with pytest.raises(moe355.Moe355Error):
+        moe355.gemm_fp8_blockscale_workspace(1, 128, 200)
 
 
 def test_zero_rows_are_noops_without_touching_memory(lib):

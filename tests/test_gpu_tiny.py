@@ -35,7 +35,7 @@ def _edge_rows(K):
     return np.stack(rows).astype(np.float32)
 
 
-@pytest.mark.parametrize("M,K", [(16, 256), (37, 1280), (1, 128), (300, 7168)])
+@pytest.mark.parametrize("M,K", [(16, 256), (37, 1280), (1, 128), (300, 7168), (19, 200), (3, 72), (40, 7176)])
 @pytest.mark.parametrize("layout", ["row", "kblock"])
 def test_quant_bitexact(m, M, K, layout):
     print("quant", M, K, layout, flush=True)
@@ -241,6 +241,43 @@ def test_dense_small(m, M, N, K, layout, split):
     torch.cuda.synchronize()
     ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
     assert_rel_max(f32_of_bf16(c), ref, what="dense %dx%dx%d" % (M, N, K))
+
+
+# K and N off multiples of 128 (ceil-sized scales): partial N only, partial K only (16
+# bytes past the last full block), both with 128-row tiles, K below one block, split-K
+# with the partial block in the last split
+@pytest.mark.parametrize("M,N,K", [(5, 576, 1024), (37, 256, 1040), (130, 200, 208), (1, 136, 64),
+                                   (8, 1000, 4112), (64, 4104, 7184), (300, 520, 400)])
+@pytest.mark.parametrize("split", [True, False], ids=["ws", "nows"])
+def test_dense_partial_blocks(m, M, N, K, split):
+    from fp8_block_scaled_grouped_amd import inputs
+    print("dense partial", M, N, K, split, flush=True)
+    d = inputs.make_dense_inputs(M, N, K, "cpu", seed=M + 7 * N + K)
+    x = f32_of_bf16(d["a"])
+    a8, sa = oracle.quant.quant_1x128(x)
+    # the library's own quantisation of the partial last group agrees bit for bit
+    q_dev, s_dev = m.fp8_quant_1x128(d["a"].to(DEV))
+    c = m.gemm_fp8_blockscale(torch.from_numpy(a8).to(DEV), torch.from_numpy(sa).to(DEV), d["b"].to(DEV),
+                              d["b_scale"].to(DEV), workspace=None if split else False)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_u8(q_dev), a8)
+    assert np.array_equal(s_dev.cpu().numpy().view(np.uint32), sa.view(np.uint32))
+    ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
+    assert_rel_max(f32_of_bf16(c), ref, what="dense partial %dx%dx%d" % (M, N, K))
+
+
+def test_dense_partial_n_leaves_padding_columns(m):
+    # c with a wider row stride: columns past N keep their contents
+    from fp8_block_scaled_grouped_amd import inputs
+    M, N, K = 20, 264, 336
+    d = inputs.make_dense_inputs(M, N, K, DEV, seed=11)
+    a8, sa = m.fp8_quant_1x128(d["a"])
+    cbuf = torch.full((M, 512), 5.0, dtype=torch.bfloat16, device=DEV)
+    m.gemm_fp8_blockscale(a8, sa, d["b"], d["b_scale"], c=cbuf[:, :N])
+    c2 = m.gemm_fp8_blockscale(a8, sa, d["b"], d["b_scale"])
+    torch.cuda.synchronize()
+    assert bool((cbuf[:, N:] == 5.0).all())
+    assert torch.equal(cbuf[:, :N].view(torch.int16), c2.view(torch.int16))
 
 
 def test_dense_split_deterministic(m):
