@@ -30,8 +30,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "tiny", "dense"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "skew", "tiny", "dense", "prefill_bias0", "skew_zipf"],
+                    help="prefill_bias0 / skew_zipf: labelled routing controls (zero bias; Zipf without the hot bias)")
     ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--preshuffle", action="store_true",
+                    help="weights permuted once into the 128x128-tile layout (the *_wpreshuffle calls)")
     ap.add_argument("--dense-m", type=int, default=64)
     ap.add_argument("--dense-n", type=int, default=18432)
     ap.add_argument("--seed", type=int, default=0)
@@ -157,7 +161,7 @@ def bench_moe(a):
     import fp8_block_scaled_grouped_amd as m
     from fp8_block_scaled_grouped_amd import inputs
 
-    cfg = inputs.MOE_CONFIGS[a.workload]
+    cfg = {**inputs.MOE_CONFIGS, **inputs.CONTROL_CONFIGS}[a.workload]
     bm = a.block_m or cfg.block_m
     dev = torch.device("cuda:0")
     t0 = time.time()
@@ -165,7 +169,8 @@ def bench_moe(a):
     x = {k: v.to(dev) for k, v in x.items()}
     torch.cuda.synchronize()
     gen_s = time.time() - t0
-    layer = m.MoELayer(cfg, x["bias"], x["w1"], x["w1_scale"], x["w2"], x["w2_scale"], block_m=bm)
+    layer = m.MoELayer(cfg, x["bias"], x["w1"], x["w1_scale"], x["w2"], x["w2_scale"], block_m=bm,
+                       preshuffle=a.preshuffle)
     hidden, logits = x["hidden"], x["logits"]
 
     stream = torch.cuda.current_stream()
@@ -186,10 +191,10 @@ def bench_moe(a):
         m.fp8_quant_1x128(hidden, layer.a8, layer.a_scale)
         ev[i][0].record(stream)
         m.moe_fp8_blockscale_g1u1(layer.a8, layer.a_scale, layer.w1, layer.w1_scale, sid, seid, nv, c.topk, bm,
-                                  layer.h8, layer.h_scale)
+                                  layer.h8, layer.h_scale, preshuffled=layer.preshuffle)
         ev[i][1].record(stream)
         m.moe_down_combine(layer.h8, layer.h_scale, layer.w2, layer.w2_scale, sid, sw, seid, nv, layer.T, c.topk,
-                           bm, layer.out, layer.down_ws)
+                           bm, layer.out, layer.down_ws, preshuffled=layer.preshuffle)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / a.steps
@@ -203,10 +208,11 @@ def bench_moe(a):
         ("fp8_quant_1x128", lambda: m.fp8_quant_1x128(hidden, layer.a8, layer.a_scale)),
         ("moe_fp8_blockscale_g1u1", lambda: m.moe_fp8_blockscale_g1u1(layer.a8, layer.a_scale, layer.w1,
                                                                       layer.w1_scale, sid, seid, nv, c.topk, bm,
-                                                                      layer.h8, layer.h_scale)),
+                                                                      layer.h8, layer.h_scale,
+                                                                      preshuffled=layer.preshuffle)),
         ("moe_down_combine", lambda: m.moe_down_combine(layer.h8, layer.h_scale, layer.w2, layer.w2_scale, sid, sw,
                                                         seid, nv, layer.T, c.topk, bm, layer.out,
-                                                        layer.down_ws)),
+                                                        layer.down_ws, preshuffled=layer.preshuffle)),
     ]
     reps = max(10, a.steps)
     cev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
@@ -254,14 +260,16 @@ def bench_moe(a):
         "config": {"workload": "%s MoE layer: %d tokens, hidden %d, intermediate %d, %d experts / %d groups, "
                                "topk_group %d, top-%d, block_m %d" % (a.workload, T, H, I, cfg.E, cfg.n_group,
                                                                       cfg.topk_group, k, bm),
-                   "tokens": T, "hidden": H, "intermediate": I, "experts": cfg.E, "topk": k, "block_m": bm},
+                   "tokens": T, "hidden": H, "intermediate": I, "experts": cfg.E, "topk": k, "block_m": bm,
+                   "preshuffled_weights": bool(a.preshuffle)},
         "layer_tflops": flops / (ms * 1e-3) / 1e12, "layer_gbs": nbytes / (ms * 1e-3) / 1e9,
         "layer_frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
         "routing": rs, "roofline": roof, "per_call_ms": per_call, "input_gen_s": round(gen_s, 2),
     }
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_moe(cfg, hidden, logits, layer.bias, layer.w1, layer.w1_scale, layer.w2,
+        # the oracle reads the weights as loaded (row-major), not the layer's shuffled copies
+        res["cpu_baseline"] = cpu_baseline_moe(cfg, hidden, logits, layer.bias, x["w1"], layer.w1_scale, x["w2"],
                                                layer.w2_scale, a.cpu_seconds)
     return res
 
@@ -278,6 +286,8 @@ def bench_dense(a):
     # rotate distinct weight copies so a small B is not served from the 256 MB MALL
     ncopy = max(1, min(48, (1 << 30) // (N * K)))
     bs = [d["b"]] + [d["b"].clone() for _ in range(ncopy - 1)]
+    if a.preshuffle:
+        bs = [m.shuffle_weight_128x128(b) for b in bs]
     a8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
     sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -285,14 +295,14 @@ def bench_dense(a):
     ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else False
     for i in range(a.warmup):
         m.fp8_quant_1x128(d["a"], a8, sa)
-        m.gemm_fp8_blockscale(a8, sa, bs[i % ncopy], d["b_scale"], c, workspace=ws)
+        m.gemm_fp8_blockscale(a8, sa, bs[i % ncopy], d["b_scale"], c, workspace=ws, preshuffled=a.preshuffle)
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(a.steps):
         m.fp8_quant_1x128(d["a"], a8, sa)
-        m.gemm_fp8_blockscale(a8, sa, bs[i % ncopy], d["b_scale"], c, workspace=ws)
+        m.gemm_fp8_blockscale(a8, sa, bs[i % ncopy], d["b_scale"], c, workspace=ws, preshuffled=a.preshuffle)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / a.steps
@@ -301,7 +311,7 @@ def bench_dense(a):
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     g0.record(stream)
     for i in range(a.steps):
-        m.gemm_fp8_blockscale(a8, sa, bs[(i + 1) % ncopy], d["b_scale"], c, workspace=ws)
+        m.gemm_fp8_blockscale(a8, sa, bs[(i + 1) % ncopy], d["b_scale"], c, workspace=ws, preshuffled=a.preshuffle)
     g1.record(stream)
     torch.cuda.synchronize()
     gms = g0.elapsed_time(g1) / a.steps
@@ -318,7 +328,8 @@ def bench_dense(a):
             "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic",
             "config": {"workload": "dense FP8 block-scale GEMM M=%d N=%d K=%d (quant + GEMM)" % (M, N, K),
-                       "M": M, "N": N, "K": K, "weight_copies": ncopy, "split_k_workspace_bytes": nws},
+                       "M": M, "N": N, "K": K, "weight_copies": ncopy, "split_k_workspace_bytes": nws,
+                       "preshuffled_weights": bool(a.preshuffle)},
             "roofline": roof}
 
 

@@ -19,4 +19,5 @@ from .moe355 import (  # noqa: F401
     moe_fp8_blockscale_g1u1,
     moe_sort,
     moe_sort_sizes,
+    shuffle_weight_128x128,
 )

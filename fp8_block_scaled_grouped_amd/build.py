@@ -6,6 +6,7 @@ Every source under csrc/ is compiled on each call (no staleness check), so
 the library always matches the tree.
 """
 import argparse
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -14,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe355.so")
-SOURCES = ["topk.hip", "sort.hip", "quant.hip", "gemm.hip", "status.cpp"]
+SOURCES = ["gemm.hip", "topk.hip", "sort.hip", "quant.hip", "shuffle.hip", "status.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # per-source extra flags: MFMA results in VGPRs so the fp32 fold reads them directly
@@ -29,27 +30,31 @@ HIP_FLAGS = [
 ]
 
 
+def _compile(src, save_temps, verbose):
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(CSRC, "_obj", src + ".o")
+    os.makedirs(os.path.dirname(obj), exist_ok=True)
+    cmd = [HIPCC] + HIP_FLAGS + EXTRA.get(src, []) + ["-c", path, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-c", path, "-o", obj]
+    if save_temps and src.endswith(".hip"):
+        os.makedirs(save_temps, exist_ok=True)
+        cmd += ["-save-temps=obj"]
+        cmd[cmd.index("-o") + 1] = os.path.join(save_temps, src + ".o")
+        obj = cmd[cmd.index("-o") + 1]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on " + src)
+    return obj
+
+
 def build(save_temps=None, verbose=False):
-    objs = []
-    for src in SOURCES:
-        path = os.path.join(CSRC, src)
-        obj = os.path.join(CSRC, "_obj", src + ".o")
-        os.makedirs(os.path.dirname(obj), exist_ok=True)
-        cmd = [HIPCC] + HIP_FLAGS + EXTRA.get(src, []) + ["-c", path, "-o", obj]
-        if src.endswith(".cpp"):
-            cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-c", path, "-o", obj]
-        if save_temps and src.endswith(".hip"):
-            os.makedirs(save_temps, exist_ok=True)
-            cmd += ["-save-temps=obj"]
-            cmd[cmd.index("-o") + 1] = os.path.join(save_temps, src + ".o")
-            obj = cmd[cmd.index("-o") + 1]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            sys.stderr.write(r.stdout + r.stderr)
-            raise RuntimeError("hipcc failed on " + src)
-        objs.append(obj)
+    # the sources compile independently (gemm.hip, the longest, first)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(lambda src: _compile(src, save_temps, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -173,9 +173,19 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r0, int lane) {
 // K % 128 bytes of each row.  Its chunks past K are fetched from the row's
 // first chunk (in bounds) and overwritten with zeros in LDS once the stage has
 // landed, so they add nothing to the block sum.
-template <class C, int MODE, bool PK = false>
+//
+// BSH: B is stored pre-shuffled (shuffle_weight_128x128): 128-row x 128-byte tiles,
+// the K blocks of a row tile one after another, each row's 16-byte chunks already in
+// their LDS slots, so every B DMA moves one contiguous 1 KB block.
+template <class C, int MODE, bool PK = false, bool BSH = false>
 __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   static_assert(!PK || MODE == kDense, "partial K blocks: dense mode only");
+  static_assert(!(PK && BSH), "pre-shuffled B has whole 128x128 tiles");
+  constexpr int64_t kBStep = BSH ? 128 * 128 : 128;  // bytes between K blocks of a B row
+  // pre-shuffled B blocks are 1 KB copies from the first row of 8; their offset goes
+  // in the wave-uniform address for the 128-row tiles (short of VGPRs) and in the
+  // per-lane offset for the smaller ones (short of SGPRs)
+  constexpr bool kBUni = BSH && C::BM == 128;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLds];
   __shared__ int rowinfo[C::BM];
   __shared__ float red[C::kRed][C::BM];
@@ -288,18 +298,30 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   // 1 KB block q of a region holds rows 8q .. 8q+7; lane L of its DMA moves the
   // chunk of row 8q + L/8 that belongs in slot L%8
   // (A blocks come first and B blocks follow, so block q sits at q * 1 KB of a stage)
+  // (kAQ is a multiple of NW, so DMA j of every wave moves A rows iff j < kJA)
   static_assert(C::kAOff == 0 && C::kBOff == C::kAQ * 1024, "stage layout");
+  static_assert(C::kAQ % C::NW == 0, "A/B split of the DMAs is the same in every wave");
+  constexpr int kJA = C::kAQ / C::NW;
   uint32_t voff[C::kQW];
 #pragma unroll
   for (int j = 0; j < C::kQW; ++j) {
     const int q = w + j * C::NW;
-    const bool is_a = q < C::kAQ;
+    const bool is_a = BSH ? j < kJA : q < C::kAQ;
     const int qq = is_a ? q : q - C::kAQ;
     const int r = qq * 8 + (lane >> 3);
     const int ch = (lane & 7) ^ (r & 7);
-    voff[j] = is_a ? (uint32_t)(a_row(r < C::BM ? r : 0) * g.K + ch * 16)
-                   : (uint32_t)((int64_t)b_row(r) * g.K + ch * 16);
+    if (is_a) {
+      voff[j] = (uint32_t)(a_row(r < C::BM ? r : 0) * g.K + ch * 16);
+    } else if constexpr (kBUni) {
+      voff[j] = 0;  // unused: addressed from the wave-uniform base
+    } else if constexpr (BSH) {
+      const int br0 = b_row(qq * 8);
+      voff[j] = (uint32_t)((int64_t)(br0 >> 7) * KBtot * (128 * 128) + (br0 & 127) * 128) + lane * 16;
+    } else {
+      voff[j] = (uint32_t)((int64_t)b_row(r) * g.K + ch * 16);
+    }
   }
+  const uint32_t lane16 = (uint32_t)lane * 16;
   const int my_row = wm * C::kWTM + (lane < C::kWTM ? lane : 0);
   const uint32_t soff = (uint32_t)(a_row(my_row) * g.ssm * 4);
   const uint8_t* s_base = uniform_ptr(g.a_scale);
@@ -316,7 +338,21 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     const int64_t kg = kbase + kb;  // K block in the whole problem
     if (j < C::kQW) {
       const int q = w + j * C::NW;
-      dma16((q < C::kAQ ? a_base : b_base) + kg * 128, voff[j], base + q * 1024);
+      if constexpr (kBUni) {
+        if (j < kJA) {
+          dma16(a_base + kg * 128, voff[j], base + q * 1024);
+        } else {
+          // 8 consecutive rows of one 128-row tile with every stored chunk already in its
+          // LDS slot: one contiguous 1 KB copy from the block's first row
+          const int br0 = b_row((q - C::kAQ) * 8);
+          const int64_t bofs = (int64_t)(br0 >> 7) * KBtot * (128 * 128) + (br0 & 127) * 128;
+          dma16(b_base + kg * kBStep + bofs, lane16, base + q * 1024);
+        }
+      } else if constexpr (BSH) {
+        dma16(j < kJA ? a_base + kg * 128 : b_base + kg * kBStep, voff[j], base + q * 1024);
+      } else {
+        dma16((q < C::kAQ ? a_base : b_base) + kg * 128, voff[j], base + q * 1024);
+      }
     } else {
       dma4(s_base + kg * g.sskb * 4, soff, base + sofs);
     }
@@ -623,25 +659,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-template <class C, int MODE, bool PK>
+template <class C, int MODE, bool PK, bool BSH>
 int launch_cfg(const GemmArgs& g, int64_t mblocks, hipStream_t stream) {
   if (MODE != kDense && g.N % C::kOutN != 0) return MOE355_EUNSUPPORTED;
   const int64_t grid = mblocks * ceil_div64(g.N, C::kOutN) * (MODE == kDense ? g.splits : 1);
   if (grid == 0) return MOE355_OK;
   MOE355_CHECK(grid < (1ll << 31), MOE355_EUNSUPPORTED);
-  hipLaunchKernelGGL((bs_gemm_kernel<C, MODE, PK>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, g);
+  hipLaunchKernelGGL((bs_gemm_kernel<C, MODE, PK, BSH>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, g);
   return launch_status();
 }
 
 // Tile choice per M tile: small tiles stream weights (decode, small M), 128-row
 // tiles with 8 waves feed the matrix cores (prefill, large M).
-template <int MODE, int BNB = 256, bool PK = false>
+template <int MODE, int BNB = 256, bool PK = false, bool BSH = false>
 int launch_gemm(const GemmArgs& g, int bm, int64_t mblocks, hipStream_t stream) {
   switch (bm) {
-    case 16: return launch_cfg<Cfg<MODE, 16, BNB, 4, 1, 4>, MODE, PK>(g, mblocks, stream);
-    case 32: return launch_cfg<Cfg<MODE, 32, BNB, 4, 1, 4>, MODE, PK>(g, mblocks, stream);
-    case 64: return launch_cfg<Cfg<MODE, 64, BNB, 4, 1, 3>, MODE, PK>(g, mblocks, stream);
-    case 128: return launch_cfg<Cfg<MODE, 128, BNB, 8, 2, 3>, MODE, PK>(g, mblocks, stream);
+    case 16: return launch_cfg<Cfg<MODE, 16, BNB, 4, 1, 4>, MODE, PK, BSH>(g, mblocks, stream);
+    case 32: return launch_cfg<Cfg<MODE, 32, BNB, 4, 1, 4>, MODE, PK, BSH>(g, mblocks, stream);
+    case 64: return launch_cfg<Cfg<MODE, 64, BNB, 4, 1, 3>, MODE, PK, BSH>(g, mblocks, stream);
+    case 128: return launch_cfg<Cfg<MODE, 128, BNB, 8, 2, 3>, MODE, PK, BSH>(g, mblocks, stream);
     default: return MOE355_EUNSUPPORTED;
   }
 }
@@ -700,12 +736,20 @@ extern "C" int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes)
   return MOE355_OK;
 }
 
-extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb,
-                                   const uint8_t* b8, const float* b_scale, int M, int N, int K, uint16_t* c,
-                                   int64_t ldc, int out_fp16, void* workspace, size_t workspace_bytes,
-                                   hipStream_t stream) {
+extern "C" int moe_down_combine_workspace(int T, int H, int topk, size_t* bytes) {
+  MOE355_CHECK(T >= 0 && H > 0 && topk > 0 && bytes, MOE355_EINVAL);
+  *bytes = (size_t)T * topk * H * sizeof(float) + 256;
+  return MOE355_OK;
+}
+
+namespace {
+
+int dense_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb, const uint8_t* b8,
+               const float* b_scale, int M, int N, int K, uint16_t* c, int64_t ldc, int out_fp16, void* workspace,
+               size_t workspace_bytes, hipStream_t stream, bool bsh) {
   MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && ldc >= N && (out_fp16 == 0 || out_fp16 == 1), MOE355_EINVAL);
   MOE355_CHECK(K % 16 == 0 && N % 8 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
+  MOE355_CHECK(!bsh || (K % 128 == 0 && N % 128 == 0), MOE355_EUNSUPPORTED);
   MOE355_CHECK((int64_t)M * K < (1ll << 32) && (int64_t)N * K < (1ll << 32), MOE355_EUNSUPPORTED);
   if (M == 0 || N == 0) return MOE355_OK;
   MOE355_CHECK(K > 0 && a8 && a_scale && b8 && b_scale && c && sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
@@ -738,7 +782,10 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
   g.part = static_cast<float*>(workspace);
   const int64_t mblocks = ceil_div64(M, plan.bm);
   int st;
-  if (K % 128 == 0) {
+  if (bsh) {
+    st = plan.bnb == 128 ? launch_gemm<kDense, 128, false, true>(g, plan.bm, mblocks, stream)
+                         : launch_gemm<kDense, 256, false, true>(g, plan.bm, mblocks, stream);
+  } else if (K % 128 == 0) {
     st = plan.bnb == 128 ? launch_gemm<kDense, 128>(g, plan.bm, mblocks, stream)
                          : launch_gemm<kDense, 256>(g, plan.bm, mblocks, stream);
   } else {
@@ -751,11 +798,10 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
   return launch_status();
 }
 
-extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb,
-                                       const uint8_t* w1, const float* w1_scale, const int32_t* sorted_ids,
-                                       const int32_t* sorted_expert_ids, const int32_t* num_valid, int T, int H,
-                                       int I, int E, int topk, int block_m, int64_t max_sorted, uint8_t* h8,
-                                       float* h_scale, const float* fc2_smooth_scale, hipStream_t stream) {
+int g1u1_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb, const uint8_t* w1,
+              const float* w1_scale, const int32_t* sorted_ids, const int32_t* sorted_expert_ids,
+              const int32_t* num_valid, int T, int H, int I, int E, int topk, int block_m, int64_t max_sorted,
+              uint8_t* h8, float* h_scale, const float* fc2_smooth_scale, hipStream_t stream, bool bsh) {
   MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0, MOE355_EINVAL);
   MOE355_CHECK(H % 128 == 0 && I % 128 == 0 && H <= 16384 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
   MOE355_CHECK((int64_t)T * H < (1ll << 32) && (int64_t)2 * I * H < (1ll << 32), MOE355_EUNSUPPORTED);
@@ -787,20 +833,14 @@ extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, 
   g.h_scale = h_scale;
   g.splits = 1;
   g.kbs = H / 128;
-  return launch_gemm<kG1U1>(g, block_m, max_sorted / block_m, stream);
+  return bsh ? launch_gemm<kG1U1, 256, false, true>(g, block_m, max_sorted / block_m, stream)
+             : launch_gemm<kG1U1>(g, block_m, max_sorted / block_m, stream);
 }
 
-extern "C" int moe_down_combine_workspace(int T, int H, int topk, size_t* bytes) {
-  MOE355_CHECK(T >= 0 && H > 0 && topk > 0 && bytes, MOE355_EINVAL);
-  *bytes = (size_t)T * topk * H * sizeof(float) + 256;
-  return MOE355_OK;
-}
-
-extern "C" int moe_down_combine(const uint8_t* h8, const float* h_scale, const uint8_t* w2, const float* w2_scale,
-                                const int32_t* sorted_ids, const float* sorted_weights,
-                                const int32_t* sorted_expert_ids, const int32_t* num_valid, int T, int H, int I,
-                                int E, int topk, int block_m, int64_t max_sorted, uint16_t* out, int64_t ld_out,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int down_gemm(const uint8_t* h8, const float* h_scale, const uint8_t* w2, const float* w2_scale,
+              const int32_t* sorted_ids, const float* sorted_weights, const int32_t* sorted_expert_ids,
+              const int32_t* num_valid, int T, int H, int I, int E, int topk, int block_m, int64_t max_sorted,
+              uint16_t* out, int64_t ld_out, void* workspace, size_t workspace_bytes, hipStream_t stream, bool bsh) {
   MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0 && ld_out >= H, MOE355_EINVAL);
   MOE355_CHECK(H % 256 == 0 && I % 128 == 0 && I <= 16384 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
   MOE355_CHECK(max_sorted * I < (1ll << 32) && (int64_t)H * I < (1ll << 32), MOE355_EUNSUPPORTED);
@@ -833,10 +873,67 @@ extern "C" int moe_down_combine(const uint8_t* h8, const float* h_scale, const u
   g.y = static_cast<float*>(workspace);
   g.splits = 1;
   g.kbs = I / 128;
-  int st = launch_gemm<kDown>(g, block_m, max_sorted / block_m, stream);
+  int st = bsh ? launch_gemm<kDown, 256, false, true>(g, block_m, max_sorted / block_m, stream)
+               : launch_gemm<kDown>(g, block_m, max_sorted / block_m, stream);
   if (st != MOE355_OK) return st;
   const int64_t threads = (int64_t)T * (H / 8);
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)ceil_div64(threads, 256)), dim3(256), 0, stream, g.y, T, topk, H,
                      out, ld_out, num_valid);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb,
+                                   const uint8_t* b8, const float* b_scale, int M, int N, int K, uint16_t* c,
+                                   int64_t ldc, int out_fp16, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return dense_gemm(a8, a_scale, sstride_m, sstride_kb, b8, b_scale, M, N, K, c, ldc, out_fp16, workspace,
+                    workspace_bytes, stream, false);
+}
+
+extern "C" int gemm_fp8_blockscale_wpreshuffle(const uint8_t* a8, const float* a_scale, int64_t sstride_m,
+                                               int64_t sstride_kb, const uint8_t* b8, const float* b_scale, int M,
+                                               int N, int K, uint16_t* c, int64_t ldc, int out_fp16,
+                                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return dense_gemm(a8, a_scale, sstride_m, sstride_kb, b8, b_scale, M, N, K, c, ldc, out_fp16, workspace,
+                    workspace_bytes, stream, true);
+}
+
+extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb,
+                                       const uint8_t* w1, const float* w1_scale, const int32_t* sorted_ids,
+                                       const int32_t* sorted_expert_ids, const int32_t* num_valid, int T, int H,
+                                       int I, int E, int topk, int block_m, int64_t max_sorted, uint8_t* h8,
+                                       float* h_scale, const float* fc2_smooth_scale, hipStream_t stream) {
+  return g1u1_gemm(a8, a_scale, sstride_m, sstride_kb, w1, w1_scale, sorted_ids, sorted_expert_ids, num_valid, T, H,
+                   I, E, topk, block_m, max_sorted, h8, h_scale, fc2_smooth_scale, stream, false);
+}
+
+extern "C" int moe_fp8_blockscale_g1u1_wpreshuffle(const uint8_t* a8, const float* a_scale, int64_t sstride_m,
+                                                   int64_t sstride_kb, const uint8_t* w1, const float* w1_scale,
+                                                   const int32_t* sorted_ids, const int32_t* sorted_expert_ids,
+                                                   const int32_t* num_valid, int T, int H, int I, int E, int topk,
+                                                   int block_m, int64_t max_sorted, uint8_t* h8, float* h_scale,
+                                                   const float* fc2_smooth_scale, hipStream_t stream) {
+  return g1u1_gemm(a8, a_scale, sstride_m, sstride_kb, w1, w1_scale, sorted_ids, sorted_expert_ids, num_valid, T, H,
+                   I, E, topk, block_m, max_sorted, h8, h_scale, fc2_smooth_scale, stream, true);
+}
+
+extern "C" int moe_down_combine(const uint8_t* h8, const float* h_scale, const uint8_t* w2, const float* w2_scale,
+                                const int32_t* sorted_ids, const float* sorted_weights,
+                                const int32_t* sorted_expert_ids, const int32_t* num_valid, int T, int H, int I,
+                                int E, int topk, int block_m, int64_t max_sorted, uint16_t* out, int64_t ld_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return down_gemm(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sorted_expert_ids, num_valid, T, H, I, E,
+                   topk, block_m, max_sorted, out, ld_out, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int moe_down_combine_wpreshuffle(const uint8_t* h8, const float* h_scale, const uint8_t* w2,
+                                            const float* w2_scale, const int32_t* sorted_ids,
+                                            const float* sorted_weights, const int32_t* sorted_expert_ids,
+                                            const int32_t* num_valid, int T, int H, int I, int E, int topk,
+                                            int block_m, int64_t max_sorted, uint16_t* out, int64_t ld_out,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return down_gemm(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sorted_expert_ids, num_valid, T, H, I, E,
+                   topk, block_m, max_sorted, out, ld_out, workspace, workspace_bytes, stream, true);
 }

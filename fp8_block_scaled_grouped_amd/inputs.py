@@ -53,6 +53,14 @@ MOE_CONFIGS = {
                       skew=True),
 }
 
+# Labelled controls beside the workloads above: prefill with a zero correction bias
+# (near-uniform routing) and the skewed workload's Zipf(1.1) popularity without the
+# +3.0 bias on its 16 most popular experts.
+CONTROL_CONFIGS = {
+    "prefill_bias0": replace(MOE_CONFIGS["prefill"], name="prefill_bias0", bias_std=0.0),
+    "skew_zipf": replace(MOE_CONFIGS["skew"], name="skew_zipf", hot_bias=0.0),
+}
+
 DENSE_K = 7168
 DENSE_SHAPES = [(m, n) for m in (1, 64, 4096) for n in (2048, 18432)]
 

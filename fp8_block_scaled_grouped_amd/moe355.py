@@ -34,7 +34,11 @@ _SIGNATURES = {
     "gemm_fp8_blockscale_workspace": ([_i32, _i32, _i32, _PSZ], _i32),
     "gemm_fp8_blockscale": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _vp, _sz, _vp],
                             _i32),
+    "shuffle_weight_128x128": ([_vp, _i64, _i32, _vp, _vp], _i32),
 }
+# the pre-shuffled-weight variants take the same arguments as their plain calls
+for _name in ("gemm_fp8_blockscale", "moe_fp8_blockscale_g1u1", "moe_down_combine"):
+    _SIGNATURES[_name + "_wpreshuffle"] = _SIGNATURES[_name]
 EXPORTED = tuple(_SIGNATURES)
 
 
@@ -187,10 +191,11 @@ def _scale_strides(a_scale, T, H, scale_layout):
 
 # ----------------------------------------------------------------- grouped GEMMs
 def moe_fp8_blockscale_g1u1(a8, a_scale, w1, w1_scale, sorted_ids, sorted_expert_ids, num_valid, topk, block_m,
-                            h8=None, h_scale=None, scale_layout="row", fc2_smooth_scale=None):
+                            h8=None, h_scale=None, scale_layout="row", fc2_smooth_scale=None, preshuffled=False):
     """Gate/up grouped GEMM + SiLU*up (* fc2_smooth_scale [E, I] if given) + 1x128 requant.
 
-    Returns (h8 [max_sorted, I], h_scale [max_sorted, I/128]).
+    Returns (h8 [max_sorted, I], h_scale [max_sorted, I/128]).  preshuffled: w1 holds
+    shuffle_weight_128x128 output (same shape).
     """
     _dev(a8, torch.uint8, "a8")
     _dev(w1, torch.uint8, "w1")
@@ -203,12 +208,13 @@ def moe_fp8_blockscale_g1u1(a8, a_scale, w1, w1_scale, sorted_ids, sorted_expert
     if h_scale is None:
         h_scale = torch.empty((ms, I // 128), dtype=torch.float32, device=a8.device)
     ssm, sskb = _scale_strides(a_scale, T, H, scale_layout)
-    _check(lib().moe_fp8_blockscale_g1u1(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(w1), _ptr(w1_scale),
-                                         _ptr(sorted_ids), _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E,
-                                         topk, block_m, ms, _ptr(h8), _ptr(h_scale),
-                                         _ptr(None if fc2_smooth_scale is None else
-                                              _dev(fc2_smooth_scale, torch.float32, "fc2_smooth_scale").contiguous()),
-                                         _stream()))
+    fn = lib().moe_fp8_blockscale_g1u1_wpreshuffle if preshuffled else lib().moe_fp8_blockscale_g1u1
+    _check(fn(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(w1), _ptr(w1_scale),
+              _ptr(sorted_ids), _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E,
+              topk, block_m, ms, _ptr(h8), _ptr(h_scale),
+              _ptr(None if fc2_smooth_scale is None else
+                   _dev(fc2_smooth_scale, torch.float32, "fc2_smooth_scale").contiguous()),
+              _stream()))
     return h8, h_scale
 
 
@@ -219,8 +225,9 @@ def moe_down_combine_workspace(T, H, topk):
 
 
 def moe_down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sorted_expert_ids, num_valid, T, topk,
-                     block_m, out=None, workspace=None):
-    """Down grouped GEMM + top-k weighted combine.  Returns bf16 [T, H]."""
+                     block_m, out=None, workspace=None, preshuffled=False):
+    """Down grouped GEMM + top-k weighted combine.  Returns bf16 [T, H].  preshuffled: w2 holds
+    shuffle_weight_128x128 output (same shape)."""
     _dev(h8, torch.uint8, "h8")
     _dev(w2, torch.uint8, "w2")
     E, H, I = w2.shape
@@ -229,10 +236,25 @@ def moe_down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sort
         out = torch.empty((T, H), dtype=torch.bfloat16, device=h8.device)
     if workspace is None:
         workspace = torch.empty(moe_down_combine_workspace(T, H, topk), dtype=torch.uint8, device=h8.device)
-    _check(lib().moe_down_combine(_ptr(h8), _ptr(h_scale), _ptr(w2), _ptr(w2_scale), _ptr(sorted_ids),
-                                  _ptr(sorted_weights), _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E, topk,
-                                  block_m, ms, _ptr(out), _rows(out, "out"), _ptr(workspace), workspace.numel(),
-                                  _stream()))
+    fn = lib().moe_down_combine_wpreshuffle if preshuffled else lib().moe_down_combine
+    _check(fn(_ptr(h8), _ptr(h_scale), _ptr(w2), _ptr(w2_scale), _ptr(sorted_ids), _ptr(sorted_weights),
+              _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E, topk, block_m, ms, _ptr(out), _rows(out, "out"),
+              _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+# ----------------------------------------------------------------- weight layout
+def shuffle_weight_128x128(w, out=None):
+    """e4m3 weights [..., R, K] (R, K multiples of 128) -> the same bytes in the
+    pre-shuffled 128x128-tile layout the *_wpreshuffle calls read (new tensor, same shape)."""
+    _dev(w, torch.uint8, "w")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    if out is None:
+        out = torch.empty_like(w)
+    _check(lib().shuffle_weight_128x128(_ptr(w), rows, K, _ptr(out), _stream()))
     return out
 
 
@@ -244,10 +266,11 @@ def gemm_fp8_blockscale_workspace(M, N, K):
 
 
 def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row", workspace=None,
-                        out_dtype=torch.bfloat16):
+                        out_dtype=torch.bfloat16, preshuffled=False):
     """a8 e4m3 [M, K] (1x128 scales), b8 e4m3 [N, K] (128x128 scales) -> [M, N] in out_dtype
     (bf16 or fp16; taken from c when c is given).  K and N need not be multiples of
-    128: a_scale [M, ceil(K/128)], b_scale [ceil(N/128), ceil(K/128)].
+    128: a_scale [M, ceil(K/128)], b_scale [ceil(N/128), ceil(K/128)].  preshuffled: b8 holds
+    shuffle_weight_128x128 output (same shape; N, K multiples of 128).
 
     workspace: None allocates what gemm_fp8_blockscale_workspace asks for; False runs
     without workspace (no split-K); or a device uint8 tensor.
@@ -269,8 +292,9 @@ def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row", wo
         workspace = torch.empty(n, dtype=torch.uint8, device=a8.device) if n else False
     ws_ptr, ws_n = (None, 0) if workspace is False else (_ptr(workspace), workspace.numel())
     ssm, sskb = _scale_strides(a_scale, M, K, scale_layout)
-    _check(lib().gemm_fp8_blockscale(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(b8), _ptr(b_scale), M, N, K, _ptr(c),
-                                     _rows(c, "c"), int(c.dtype == torch.float16), ws_ptr, ws_n, _stream()))
+    fn = lib().gemm_fp8_blockscale_wpreshuffle if preshuffled else lib().gemm_fp8_blockscale
+    _check(fn(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(b8), _ptr(b_scale), M, N, K, _ptr(c), _rows(c, "c"),
+              int(c.dtype == torch.float16), ws_ptr, ws_n, _stream()))
     return c
 
 
@@ -284,12 +308,16 @@ class MoELayer:
     """
 
     def __init__(self, cfg, bias, w1, w1_scale, w2, w2_scale, T=None, block_m=None, scale_layout="row",
-                 fc2_smooth_scale=None):
+                 fc2_smooth_scale=None, preshuffle=False):
         self.cfg = cfg
         self.T = cfg.T if T is None else T
         if block_m is None:
             block_m = cfg.block_m if cfg.block_m else moe_block_m(self.T, cfg.topk, cfg.E)
         self.block_m = block_m
+        # preshuffle: the weights are permuted once, here, into the 128x128-tile layout
+        self.preshuffle = preshuffle
+        if preshuffle:
+            w1, w2 = shuffle_weight_128x128(w1), shuffle_weight_128x128(w2)
         self.bias, self.w1, self.w1_scale, self.w2, self.w2_scale = bias, w1, w1_scale, w2, w2_scale
         self.scale_layout = scale_layout
         self.fc2_smooth_scale = fc2_smooth_scale
@@ -319,7 +347,7 @@ class MoELayer:
         sid, sw, seid, nv = moe_sort(self.topk_ids, self.topk_w, c.E, self.block_m, self.sort_out, self.sort_ws)
         fp8_quant_1x128(hidden, self.a8, self.a_scale, self.scale_layout)
         moe_fp8_blockscale_g1u1(self.a8, self.a_scale, self.w1, self.w1_scale, sid, seid, nv, c.topk, self.block_m,
-                                self.h8, self.h_scale, self.scale_layout, self.fc2_smooth_scale)
+                                self.h8, self.h_scale, self.scale_layout, self.fc2_smooth_scale, self.preshuffle)
         moe_down_combine(self.h8, self.h_scale, self.w2, self.w2_scale, sid, sw, seid, nv, self.T, c.topk,
-                         self.block_m, self.out, self.down_ws)
+                         self.block_m, self.out, self.down_ws, self.preshuffle)
         return self.out

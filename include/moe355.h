@@ -220,6 +220,51 @@ int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale,
                         void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
+/*
+ * Pre-shuffled weights ("General Linear Layer": the linear path runs on weights
+ * permuted once at load time into an MFMA-friendly order; the pages use such a
+ * layout with their pre-shuffle GEMM).  The permutation is this library's own:
+ * w [rows, K] e4m3 (rows and K multiples of 128) is written to out as 128-row x
+ * 128-byte tiles; tile (t, kb) -- rows [128t, 128t+128), bytes [128kb, 128kb+128)
+ * of each row -- starts at byte (t*K/128 + kb)*16384, and inside it row rr takes
+ * bytes [rr*128, rr*128+128) with its 16-byte chunk c in slot c ^ (rr & 7).
+ * An expert tensor [E, R, K] is passed as rows = E*R (R % 128 == 0).  Scales are
+ * not permuted.  out must not overlap w (else MOE355_EINVAL); rows or K not a
+ * multiple of 128 give MOE355_EUNSUPPORTED; w, out 16-byte aligned.
+ */
+int shuffle_weight_128x128(const uint8_t* w, int64_t rows, int K, uint8_t* out,
+                           hipStream_t stream);
+
+/*
+ * The three GEMM calls on weights in the shuffle_weight_128x128 layout: the same
+ * arguments, results and error behaviour as gemm_fp8_blockscale (b8 = shuffled
+ * [N, K]; N and K multiples of 128, else MOE355_EUNSUPPORTED),
+ * moe_fp8_blockscale_g1u1 (w1 = shuffled [E*2I, H]) and moe_down_combine
+ * (w2 = shuffled [E*H, I]).  The arithmetic and its order are unchanged, so the
+ * outputs equal those of the unshuffled calls bit for bit.
+ */
+int gemm_fp8_blockscale_wpreshuffle(const uint8_t* a8, const float* a_scale,
+                                    int64_t sstride_m, int64_t sstride_kb,
+                                    const uint8_t* b8, const float* b_scale,
+                                    int M, int N, int K, uint16_t* c, int64_t ldc, int out_fp16,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+int moe_fp8_blockscale_g1u1_wpreshuffle(const uint8_t* a8, const float* a_scale,
+                                        int64_t sstride_m, int64_t sstride_kb,
+                                        const uint8_t* w1, const float* w1_scale,
+                                        const int32_t* sorted_ids, const int32_t* sorted_expert_ids,
+                                        const int32_t* num_valid,
+                                        int T, int H, int I, int E, int topk, int block_m,
+                                        int64_t max_sorted, uint8_t* h8, float* h_scale,
+                                        const float* fc2_smooth_scale, hipStream_t stream);
+int moe_down_combine_wpreshuffle(const uint8_t* h8, const float* h_scale,
+                                 const uint8_t* w2, const float* w2_scale,
+                                 const int32_t* sorted_ids, const float* sorted_weights,
+                                 const int32_t* sorted_expert_ids, const int32_t* num_valid,
+                                 int T, int H, int I, int E, int topk, int block_m, int64_t max_sorted,
+                                 uint16_t* out, int64_t ld_out, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

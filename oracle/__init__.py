@@ -23,5 +23,6 @@ sort     per-expert bucketing padded to the M tile
 gemm     block-scaled FP8 GEMM (exact 128-term block sums, binary64)
 moe      gate/up + SiLU*up + requantisation, down projection + combine,
          and a token-major evaluation of the whole layer
+layout   the pre-shuffled 128x128-tile weight layout (a byte permutation)
 """
-from . import fp8, quant, routing, sort, gemm, moe  # noqa: F401
+from . import fp8, quant, routing, sort, gemm, moe, layout  # noqa: F401

@@ -88,6 +88,14 @@ def test_invalid_arguments_return_codes(lib):
                                      _p(), _p(), None, None) == -1
     assert L.moe_fp8_blockscale_g1u1(_p(), _p(), 2, 1, _p(), _p(), _p(), _p(), _p(), 16, 256, 100, 16, 4, 16, 304,
                                      _p(), _p(), None, None) == -2
+    # weight shuffle: rows or K off multiples of 128 -> EUNSUPPORTED; out overlapping w -> EINVAL
+    assert L.shuffle_weight_128x128(_p(), 100, 128, _p(1 << 20), None) == -2
+    assert L.shuffle_weight_128x128(_p(), 128, 200, _p(1 << 20), None) == -2
+    assert L.shuffle_weight_128x128(_p(1 << 20), 128, 128, _p((1 << 20) + 4096), None) == -1
+    assert L.shuffle_weight_128x128(None, 0, 128, None, None) == 0
+    # pre-shuffled dense weights need whole 128x128 tiles
+    assert L.gemm_fp8_blockscale_wpreshuffle(_p(), _p(), 2, 1, _p(), _p(), 4, 136, 256, _p(), 136, 0, None, 0,
+                                             None) == -2
     # down: workspace too small
     assert L.moe_down_combine(_p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16, 304, _p(),
                               256, _p(), 8, None) == -1

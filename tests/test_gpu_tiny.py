@@ -280,6 +280,55 @@ def test_dense_partial_n_leaves_padding_columns(m):
     assert torch.equal(cbuf[:, :N].view(torch.int16), c2.view(torch.int16))
 
 
+def test_shuffle_weight_bitexact(m):
+    w = np.random.default_rng(3).integers(0, 256, size=(3, 256, 384), dtype=np.uint8)
+    out = m.shuffle_weight_128x128(torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.layout.shuffle_128x128(w))
+
+
+# pre-shuffled weights: every tile shape (BM 16/64/128, 128 and 256 B rows), split-K or not;
+# the arithmetic is unchanged, so the output equals the plain call's bit for bit
+@pytest.mark.parametrize("M,N,K", [(1, 2048, 7168), (37, 384, 512), (200, 128, 256), (130, 512, 1024),
+                                   (64, 256, 4096)])
+def test_dense_preshuffled_bitwise(m, M, N, K):
+    from fp8_block_scaled_grouped_amd import inputs
+    print("dense preshuffled", M, N, K, flush=True)
+    d = inputs.make_dense_inputs(M, N, K, DEV, seed=M + N)
+    a8, sa = m.fp8_quant_1x128(d["a"])
+    bsh = m.shuffle_weight_128x128(d["b"])
+    for ws in (None, False):
+        c0 = m.gemm_fp8_blockscale(a8, sa, d["b"], d["b_scale"], workspace=ws)
+        c1 = m.gemm_fp8_blockscale(a8, sa, bsh, d["b_scale"], workspace=ws, preshuffled=True)
+        torch.cuda.synchronize()
+        assert torch.equal(c0.view(torch.int16), c1.view(torch.int16))
+    ref = oracle.gemm.gemm_blockscale(np_u8(a8), sa.cpu().numpy(), d["b"].cpu().numpy(), d["b_scale"].cpu().numpy())
+    assert_rel_max(f32_of_bf16(c1), ref, what="dense preshuffled %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("BM", [16, 32, 64, 128])
+def test_layer_tiny_preshuffled_bitwise(m, tiny, BM):
+    cfg, x = tiny
+    g = {k: v.to(DEV) for k, v in x.items()}
+    args = (cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"])
+    plain = m.MoELayer(*args, block_m=BM)
+    shuf = m.MoELayer(*args, block_m=BM, preshuffle=True)
+    a = plain.forward(g["hidden"], g["logits"]).clone()
+    b = shuf.forward(g["hidden"], g["logits"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # the requantised intermediate of every valid sorted row as well
+    P = int(plain.sort_out[3].item())
+    valid = plain.sort_out[0][:P] < cfg.T * cfg.topk
+    assert torch.equal(plain.h8[:P][valid], shuf.h8[:P][valid])
+    assert torch.equal(plain.h_scale[:P][valid], shuf.h_scale[:P][valid])
+    w, ids = oracle_routing(x, cfg)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(x["hidden"]))
+    ref, _, _, _ = oracle.moe.layer_tokens(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), x["w2"].numpy(),
+                                           x["w2_scale"].numpy(), ids, w)
+    assert_rel_max(f32_of_bf16(b), ref, what="tiny layer, pre-shuffled weights")
+
+
 def test_dense_split_deterministic(m):
     from fp8_block_scaled_grouped_amd import inputs
     M, N, K = 3, 2048, 7168

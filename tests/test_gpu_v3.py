@@ -140,6 +140,22 @@ def test_layer_sampled_tokens(m, weights, name, block_m, n_tok):
     check_requant(h8g, hsg, h_ref.reshape(-1, cfg.I))
 
 
+@pytest.mark.parametrize("name,block_m", [("decode", 16), ("prefill", 128)])
+def test_layer_preshuffled_bitwise(m, weights, name, block_m):
+    # the whole layer on load-time shuffled V3 weights equals the plain layer bit for bit
+    cfg, x = _inputs(name)
+    print("layer preshuffled", name, block_m, flush=True)
+    args = (cfg, x["bias"], weights["w1"], weights["w1_scale"], weights["w2"], weights["w2_scale"])
+    plain = m.MoELayer(*args, block_m=block_m)
+    a = plain.forward(x["hidden"], x["logits"]).clone()
+    shuf = m.MoELayer(*args, block_m=block_m, preshuffle=True)
+    b = shuf.forward(x["hidden"], x["logits"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    del shuf
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("name,block_m", [("decode", 16), ("prefill", 128)])
 def test_down_combine_stage(m, weights, name, block_m):
