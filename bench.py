@@ -34,6 +34,8 @@ def parse():
                     choices=["decode", "prefill", "skew", "tiny", "dense", "prefill_bias0", "skew_zipf"],
                     help="prefill_bias0 / skew_zipf: labelled routing controls (zero bias; Zipf without the hot bias)")
     ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the layer captured once as a HIP graph and replayed (graph_ms_per_step)")
     ap.add_argument("--preshuffle", action="store_true",
                     help="weights permuted once into the 128x128-tile layout (the *_wpreshuffle calls)")
     ap.add_argument("--dense-m", type=int, default=64)
@@ -200,6 +202,25 @@ def bench_moe(a):
     ms = start.elapsed_time(end) / a.steps
     g1u1_ms = sum(s.elapsed_time(e) for s, e in ev) / a.steps
 
+    graph = None
+    if a.graph:
+        # the five calls captured once into a HIP graph (the library allocates nothing and
+        # never synchronises, so the layer is capturable) and replayed K times
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.forward(hidden, logits)
+        for _ in range(a.warmup):
+            g.replay()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(a.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph = g0.elapsed_time(g1) / a.steps
+        del g
+
     # per-call breakdown (outside the timed region): events around each of the five calls
     calls = [
         ("grouped_topk", lambda: m.grouped_topk(logits, layer.bias, c.n_group, c.topk_group, c.topk, c.renorm,
@@ -267,6 +288,9 @@ def bench_moe(a):
         "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
         "routing": rs, "roofline": roof, "per_call_ms": per_call, "input_gen_s": round(gen_s, 2),
     }
+    if graph is not None:
+        res["graph_ms_per_step"] = graph
+        res["graph_tokens_per_s"] = T / (graph * 1e-3)
     if not a.no_cpu_baseline:
         # the oracle reads the weights as loaded (row-major), not the layer's shuffled copies
         res["cpu_baseline"] = cpu_baseline_moe(cfg, hidden, logits, layer.bias, x["w1"], layer.w1_scale, x["w2"],

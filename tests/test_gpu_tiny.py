@@ -329,6 +329,28 @@ def test_layer_tiny_preshuffled_bitwise(m, tiny, BM):
     assert_rel_max(f32_of_bf16(b), ref, what="tiny layer, pre-shuffled weights")
 
 
+@pytest.mark.parametrize("BM", [16, 128])
+def test_layer_graph_replay_matches_eager(m, tiny, BM):
+    # the five calls allocate nothing and never synchronise: captured once as a graph, every
+    # replay (with eager work and synchronisations between replays) reproduces the eager output
+    cfg, x = tiny
+    g = {k: v.to(DEV) for k, v in x.items()}
+    layer = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"], block_m=BM)
+    eager = layer.forward(g["hidden"], g["logits"]).clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward(g["hidden"], g["logits"])
+    for i in range(3):
+        layer.out.fill_(float(i + 7))
+        other = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"], block_m=16)
+        other.forward(g["hidden"], g["logits"])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out.view(torch.int16), eager.view(torch.int16)), "replay %d" % i
+
+
 def test_dense_split_deterministic(m):
     from fp8_block_scaled_grouped_amd import inputs
     M, N, K = 3, 2048, 7168
