@@ -28,7 +28,7 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "skew", "tiny", "dense", "prefill_bias0", "skew_zipf"],
@@ -182,11 +182,13 @@ def bench_moe(a):
 
     # timed region: K whole steps; the dominant kernel (g1u1) bracketed by events inside it
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]  # start of each step
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c = cfg
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(a.steps):
+        st[i].record(stream)
         m.grouped_topk(logits, layer.bias, c.n_group, c.topk_group, c.topk, c.renorm, c.routed_scaling_factor,
                        layer.topk_w, layer.topk_ids)
         sid, sw, seid, nv = m.moe_sort(layer.topk_ids, layer.topk_w, c.E, bm, layer.sort_out, layer.sort_ws)
@@ -201,6 +203,8 @@ def bench_moe(a):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / a.steps
     g1u1_ms = sum(s.elapsed_time(e) for s, e in ev) / a.steps
+    steps_ms = sorted([st[i].elapsed_time(st[i + 1]) for i in range(a.steps - 1)] + [st[-1].elapsed_time(end)])
+    layer_stats = {"median_ms": steps_ms[len(steps_ms) // 2], "min_ms": steps_ms[0]}
 
     graph = None
     if a.graph:
@@ -286,7 +290,8 @@ def bench_moe(a):
         "layer_tflops": flops / (ms * 1e-3) / 1e12, "layer_gbs": nbytes / (ms * 1e-3) / 1e9,
         "layer_frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
-        "routing": rs, "roofline": roof, "per_call_ms": per_call, "input_gen_s": round(gen_s, 2),
+        "routing": rs, "roofline": roof, "layer_ms": layer_stats, "per_call_ms": per_call,
+        "input_gen_s": round(gen_s, 2),
     }
     if graph is not None:
         res["graph_ms_per_step"] = graph
