@@ -170,9 +170,10 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r0, int lane) {
 }
 
 // PK (dense only): K is not a multiple of 128, so the last K block holds
-// K % 128 bytes of each row.  Its chunks past K are fetched from the row's
-// first chunk (in bounds) and overwritten with zeros in LDS once the stage has
-// landed, so they add nothing to the block sum.
+// K % 128 bytes of each row.  The DMA pipeline walks the full blocks; the
+// workgroup that owns the last block then loads it through registers into
+// stage 0 with its chunks past K written as zeros (they add nothing to the
+// block sum) and runs one more K step on it.
 //
 // BSH: B is stored pre-shuffled (shuffle_weight_128x128): 128-row x 128-byte tiles,
 // the K blocks of a row tile one after another, each row's 16-byte chunks already in
