@@ -203,3 +203,54 @@ def test_dense_full_shapes(m, M, N):
     assert np.array_equal(np_u8(a8)[rows], ar)
     ref = oracle.gemm.gemm_blockscale(ar, sr, np_u8(d["b"]), d["b_scale"].cpu().numpy())
     assert_rel_max(f32_of_bf16(c[torch.from_numpy(rows).to(DEV)]), ref, what="dense %dx%d" % (M, N))
+
+
+@pytest.mark.timeout(300)
+def test_dense_largest_operand(m):
+    # M*K just under 2^32: the 32-bit per-lane DMA offsets into A and the quantisation's
+    # group indexing at their limit (A is 8.6 GB of bf16, 4.3 GB of e4m3)
+    from fp8_block_scaled_grouped_amd import inputs
+    K, N = 16384, 256
+    M = (1 << 32) // K - 1
+    print("dense largest", M, N, K, flush=True)
+    d = inputs.make_dense_inputs(M, N, K, DEV, seed=3)
+    a8, sa = m.fp8_quant_1x128(d["a"])
+    c = m.gemm_fp8_blockscale(a8, sa, d["b"], d["b_scale"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, M // 2, M - 2, M - 1], rng.integers(0, M, 11)]))
+    rt = torch.from_numpy(rows).to(DEV)
+    ar, sr = oracle.quant.quant_1x128(f32_of_bf16(d["a"][rt]))
+    assert np.array_equal(np_u8(a8[rt]), ar)
+    assert np.array_equal(sa[rt].cpu().numpy().view(np.uint32), sr.view(np.uint32))
+    ref = oracle.gemm.gemm_blockscale(ar, sr, np_u8(d["b"]), d["b_scale"].cpu().numpy())
+    assert_rel_max(f32_of_bf16(c[rt]), ref, what="dense %dx%dx%d" % (M, N, K))
+    del d, a8, sa, c
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(300)
+def test_grouped_gemms_largest_operand(m):
+    # T*H just under 2^32 (hidden 16384, the largest the grouped calls take): the gathered A
+    # rows' 32-bit DMA offsets at their limit, 17 GB of per-pair down staging
+    from fp8_block_scaled_grouped_amd import inputs
+    H, I = 16384, 128
+    T = (1 << 32) // H - 144
+    cfg = inputs.MoEConfig("largest", T=T, H=H, I=I, E=4, n_group=2, topk_group=1, topk=1, block_m=128)
+    print("moe largest", T, H, I, flush=True)
+    x = inputs.make_moe_inputs(cfg, DEV, seed=4)
+    layer = m.MoELayer(cfg, x["bias"], x["w1"], x["w1_scale"], x["w2"], x["w2_scale"])
+    out = layer.forward(x["hidden"], x["logits"])
+    torch.cuda.synchronize()
+    w, ids = oracle.routing.grouped_topk(x["logits"].cpu().numpy(), x["bias"].cpu().numpy(), cfg.n_group,
+                                         cfg.topk_group, cfg.topk, cfg.renorm, cfg.routed_scaling_factor)
+    assert np.array_equal(layer.topk_ids.cpu().numpy(), ids)
+    rng = np.random.default_rng(4)
+    tok = np.unique(np.concatenate([[0, T // 2, T - 2, T - 1], rng.integers(0, T, 8)]))
+    tt = torch.from_numpy(tok).to(DEV)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(x["hidden"][tt]))
+    ref, _, _, _ = oracle.moe.layer_tokens(a8, sa, x["w1"].cpu().numpy(), x["w1_scale"].cpu().numpy(),
+                                           x["w2"].cpu().numpy(), x["w2_scale"].cpu().numpy(), ids[tok], w[tok])
+    assert_rel_max(f32_of_bf16(out[tt]), ref, what="largest grouped layer")
+    del layer, x, out
+    torch.cuda.empty_cache()
