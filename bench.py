@@ -313,7 +313,7 @@ def bench_dense(a):
     dev = torch.device("cuda:0")
     d = inputs.make_dense_inputs(M, N, K, dev, seed=a.seed)
     # rotate distinct weight copies so a small B is not served from the 256 MB MALL
-    ncopy = max(1, min(48, (1 << 30) // (N * K)))
+    ncopy = max(1, min(48, (8 << 30) // (N * K)))  # >= 40 copies below 200 MB of weights
     bs = [d["b"]] + [d["b"].clone() for _ in range(ncopy - 1)]
     if a.preshuffle:
         bs = [m.shuffle_weight_128x128(b) for b in bs]
