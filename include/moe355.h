@@ -38,7 +38,7 @@ extern "C" {
 #define MOE355_OK 0
 #define MOE355_EINVAL (-1)       /* null pointer, negative size, ld < width, workspace too small */
 #define MOE355_EUNSUPPORTED (-2) /* shape or option outside what the kernels implement */
-#define MOE355_EMISALIGNED (-3)  /* a base pointer or row stride breaks the 16-byte alignment rule */
+#define MOE355_EMISALIGNED (-3)  /* a base pointer or row stride breaks the call's alignment rule */
 #define MOE355_ELAUNCH (-4)      /* the HIP runtime reported an error at launch */
 
 /* Human-readable text of a status code (static storage; never NULL). */
