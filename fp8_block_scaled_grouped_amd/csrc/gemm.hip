@@ -250,7 +250,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   }
 
   // this wave's B scales for every K block, fetched before the DMA pipeline starts:
-  // lane L holds blocks L and L + 64 (K <= 16384); read per step with readlane
+  // lane L holds blocks L and L + 64 (a workgroup walks at most 128); read per step with readlane
   const float sbv0 = lane < KB ? sbp[lane] : 0.0f;
   const float sbv1 = lane + 64 < KB ? sbp[lane + 64] : 0.0f;
 
@@ -621,13 +621,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // c[m, n] = bf16 (or fp16) of the fp32 sum of part[split, m, n] over the splits, in a fixed
 // order: wave w sums splits w, w+4, w+8, ... in ascending order, then the four
 // wave sums are added in wave order.  One workgroup covers 256 columns of one
-// row; every lane keeps up to 8 loads in flight.
+// row (workgroup b: row b / ceil(N/256), column block b % ceil(N/256)); every lane
+// keeps up to 8 loads in flight.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
                                                             uint16_t* __restrict__ c, int64_t ldc, int out_f16) {
   __shared__ float sh[4][256];
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int m = blockIdx.y;
-  const int col = blockIdx.x * 256 + lane * 4;
+  const int nbn = (N + 255) / 256;
+  const int m = (int)(blockIdx.x / nbn);
+  const int col = (int)(blockIdx.x % nbn) * 256 + lane * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (col < N) {
     const float* p = part + (int64_t)m * N + col;
@@ -689,8 +691,11 @@ int launch_gemm(const GemmArgs& g, int bm, int64_t mblocks, hipStream_t stream) 
 // loops per workgroup lose more to pipeline fill and epilogue than a second
 // round of workgroups gains.  The fp32 partials (written once, read once) are
 // capped at 1/kSplitBytesDiv of the weight bytes: splits * M * N * 4 <= N * K /
-// kSplitBytesDiv.  Each split walks at least two K blocks.
+// kSplitBytesDiv.  Each split walks at least two K blocks.  A workgroup holds the
+// weight scales of at most kMaxKbs K blocks (two per lane), so K beyond 128 blocks
+// is always split, whatever M.
 constexpr int64_t kSplitTargetWG = 256;
+constexpr int kMaxKbs = 128;
 constexpr int64_t kSplitBytesDiv = 4;
 constexpr int kNarrowMaxN = 4096;  // M <= 64: 128-column tiles up to this N, 256 above
 
@@ -709,6 +714,7 @@ DensePlan dense_plan(int M, int N, int K) {
     const int64_t by_bytes = std::max<int64_t>(1, K / (kSplitBytesDiv * 4 * M));
     splits = (int)std::min<int64_t>({(int64_t)KB / 2, kSplitTargetWG / base, by_bytes});
   }
+  splits = std::max(splits, (int)ceil_div64(KB, kMaxKbs));
   p.kbs = (int)ceil_div64(KB, splits);
   p.splits = (int)ceil_div64(KB, p.kbs);
   return p;
@@ -732,7 +738,7 @@ using namespace moe355;
 
 extern "C" int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes) {
   MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && bytes, MOE355_EINVAL);
-  MOE355_CHECK(K % 16 == 0 && N % 8 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
+  MOE355_CHECK(K % 16 == 0 && N % 8 == 0, MOE355_EUNSUPPORTED);
   *bytes = (M == 0 || N == 0 || K == 0) ? 0 : dense_workspace_bytes(dense_plan(M, N, K), M, N);
   return MOE355_OK;
 }
@@ -749,7 +755,7 @@ int dense_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64
                const float* b_scale, int M, int N, int K, uint16_t* c, int64_t ldc, int out_fp16, void* workspace,
                size_t workspace_bytes, hipStream_t stream, bool bsh) {
   MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && ldc >= N && (out_fp16 == 0 || out_fp16 == 1), MOE355_EINVAL);
-  MOE355_CHECK(K % 16 == 0 && N % 8 == 0 && K <= 16384, MOE355_EUNSUPPORTED);
+  MOE355_CHECK(K % 16 == 0 && N % 8 == 0, MOE355_EUNSUPPORTED);
   MOE355_CHECK(!bsh || (K % 128 == 0 && N % 128 == 0), MOE355_EUNSUPPORTED);
   MOE355_CHECK((int64_t)M * K < (1ll << 32) && (int64_t)N * K < (1ll << 32), MOE355_EUNSUPPORTED);
   if (M == 0 || N == 0) return MOE355_OK;
@@ -759,7 +765,9 @@ int dense_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64
   DensePlan plan = dense_plan(M, N, K);
   const size_t need = dense_workspace_bytes(plan, M, N);
   if (need == 0 || workspace == nullptr || workspace_bytes < need) {
-    // without (enough) workspace: one workgroup per output tile walks all of K
+    // without (enough) workspace: one workgroup per output tile walks all of K, which
+    // holds the weight scales of at most kMaxKbs K blocks
+    MOE355_CHECK(ceil_div64(K, 128) <= kMaxKbs, need > 0 && workspace != nullptr ? MOE355_EINVAL : MOE355_EUNSUPPORTED);
     plan.splits = 1;
     plan.kbs = (int)ceil_div64(K, 128);
   } else {
@@ -794,8 +802,10 @@ int dense_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64
                          : launch_gemm<kDense, 256, true>(g, plan.bm, mblocks, stream);
   }
   if (st != MOE355_OK || plan.splits == 1) return st;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)ceil_div64(N, 256), (unsigned)M), dim3(256), 0, stream,
-                     g.part, plan.splits, M, N, c, ldc, out_fp16);
+  const int64_t rblocks = ceil_div64(N, 256) * M;
+  MOE355_CHECK(rblocks < (1ll << 31), MOE355_EUNSUPPORTED);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)rblocks), dim3(256), 0, stream, g.part, plan.splits, M, N, c,
+                     ldc, out_fp16);
   return launch_status();
 }
 

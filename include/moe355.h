@@ -210,8 +210,10 @@ int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes);
  * workspace device memory of gemm_fp8_blockscale_workspace() bytes, or NULL / 0: small M
  *          then splits K over more workgroups, keeps fp32 partial sums there and adds them
  *          in a fixed order (deterministic); without it one workgroup per output
- *          tile walks all of K.  Contents need no initialisation.
- * K % 16 == 0, N % 8 == 0, K <= 16384 (else MOE355_EUNSUPPORTED); a8, b8 16-byte aligned.
+ *          tile walks all of K.  Contents need no initialisation.  K above 16384 (more
+ *          than 128 K blocks) is always split and needs the workspace: without it
+ *          MOE355_EUNSUPPORTED, with too little MOE355_EINVAL.
+ * K % 16 == 0, N % 8 == 0 (else MOE355_EUNSUPPORTED); a8, b8 16-byte aligned.
  */
 int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale,
                         int64_t sstride_m, int64_t sstride_kb,

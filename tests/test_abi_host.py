@@ -76,6 +76,9 @@ def test_invalid_arguments_return_codes(lib):
     assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 100, 256, _p(), 104, 0, None, 0, None) == -2
     assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 200, _p(), 128, 0, None, 0, None) == -2
     assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 120, 0, None, 0, None) == -1
+    # K above 16384 needs the split-K workspace: none -> EUNSUPPORTED, too little -> EINVAL
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 300, 256, 18432, _p(), 256, 0, None, 0, None) == -2
+    assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 300, 256, 18432, _p(), 256, 0, _p(), 64, None) == -1
     assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 64, 0, None, 0, None) == -1
     # output type flag must be 0 or 1; logits type flag likewise
     assert L.gemm_fp8_blockscale(_p(), _p(), 2, 1, _p(), _p(), 4, 128, 256, _p(), 128, 2, None, 0, None) == -1
@@ -113,6 +116,9 @@ def test_dense_workspace_query(lib):
     assert moe355.gemm_fp8_blockscale_workspace(1, 2048, 256) == 0  # two K blocks: nothing to split
     # partial blocks: K and N in ceil(./128) blocks
     assert moe355.gemm_fp8_blockscale_workspace(1, 1000, 4112) > 0
+    # more than 128 K blocks always splits, whatever M
+    assert moe355.gemm_fp8_blockscale_workspace(4096, 7168, 18432) >= 2 * 4096 * 7168 * 4
+    assert moe355.gemm_fp8_blockscale_workspace(4096, 7168, 16384) == 0
     with pytest.raises(moe355.Moe355Error):
         moe355.gemm_fp8_blockscale_workspace(1, 100, 256)
     with pytest.raises(moe355.Moe355Error):

@@ -266,6 +266,25 @@ def test_dense_partial_blocks(m, M, N, K, split):
     assert_rel_max(f32_of_bf16(c), ref, what="dense partial %dx%dx%d" % (M, N, K))
 
 
+# more than 128 K blocks: always split (a workgroup holds the scales of at most 128),
+# also at M above 64; with partial N / K as well
+@pytest.mark.parametrize("M,N,K", [(37, 256, 18432), (300, 512, 16512), (1, 576, 24576), (130, 136, 16400)])
+def test_dense_long_k(m, M, N, K):
+    from fp8_block_scaled_grouped_amd import inputs
+    print("dense long K", M, N, K, flush=True)
+    assert m.gemm_fp8_blockscale_workspace(M, N, K) > 0
+    d = inputs.make_dense_inputs(M, N, K, "cpu", seed=M + N + K)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(d["a"]))
+    c = m.gemm_fp8_blockscale(torch.from_numpy(a8).to(DEV), torch.from_numpy(sa).to(DEV), d["b"].to(DEV),
+                              d["b_scale"].to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
+    assert_rel_max(f32_of_bf16(c), ref, what="dense long K %dx%dx%d" % (M, N, K))
+    with pytest.raises(m.Moe355Error):
+        m.gemm_fp8_blockscale(torch.from_numpy(a8).to(DEV), torch.from_numpy(sa).to(DEV), d["b"].to(DEV),
+                              d["b_scale"].to(DEV), workspace=False)
+
+
 def test_dense_partial_n_leaves_padding_columns(m):
     # c with a wider row stride: columns past N keep their contents
     from fp8_block_scaled_grouped_amd import inputs
