@@ -85,6 +85,15 @@ def _dev(t, dtype, name):
     return t
 
 
+def _need(t, shape, dtype, name):
+    """A contiguous device tensor of exactly this shape and dtype (the kernels index it densely)."""
+    _dev(t, dtype, name)
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s, got %s" % (name, dtype, tuple(shape),
+                                                                                 tuple(t.shape)))
+    return t
+
+
 def _rows(t, name):
     """Row stride of a 2-D tensor whose rows are contiguous."""
     if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
@@ -103,17 +112,21 @@ def grouped_topk(logits, bias, n_group, topk_group, topk, renorm, routed_scaling
     if logits.dtype != torch.bfloat16:
         _dev(logits, torch.float32, "logits")
     _dev(logits, logits.dtype, "logits")
-    _dev(bias, torch.float32, "bias")
     T, E = logits.shape
+    _need(bias, (E,), torch.float32, "bias")
     if topk_weights is None:
         topk_weights = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
     if topk_ids is None:
         topk_ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+    _dev(topk_weights, torch.float32, "topk_weights")
+    _dev(topk_ids, torch.int32, "topk_ids")
+    if tuple(topk_weights.shape) != (T, topk) or tuple(topk_ids.shape) != (T, topk):
+        raise ValueError("top-k outputs must be [T, topk] = %s" % ((T, topk),))
     ld = _rows(topk_weights, "topk_weights")
     if _rows(topk_ids, "topk_ids") != ld:
         raise ValueError("topk_weights and topk_ids must share a row stride")
     _check(lib().grouped_topk(_ptr(logits), int(logits.dtype == torch.bfloat16), _rows(logits, "logits"),
-                              _ptr(bias.contiguous()), T, E, n_group,
+                              _ptr(bias), T, E, n_group,
                               topk_group, topk, int(bool(renorm)), float(routed_scaling_factor),
                               _ptr(topk_weights), _ptr(topk_ids), ld, _stream()))
     return topk_weights, topk_ids
@@ -139,6 +152,8 @@ def moe_sort(topk_ids, topk_weights, E, block_m, out=None, workspace=None):
     _dev(topk_ids, torch.int32, "topk_ids")
     _dev(topk_weights, torch.float32, "topk_weights")
     T, k = topk_ids.shape
+    if tuple(topk_weights.shape) != (T, k):
+        raise ValueError("topk_weights must have the shape of topk_ids")
     ms, mb, wsb = moe_sort_sizes(T, k, E, block_m)
     dev = topk_ids.device
     if out is None:
@@ -147,6 +162,12 @@ def moe_sort(topk_ids, topk_weights, E, block_m, out=None, workspace=None):
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     sid, sw, seid, nv = out
+    for t, n, dt, name in ((sid, ms, torch.int32, "sorted_ids"), (sw, ms, torch.float32, "sorted_weights"),
+                           (seid, mb, torch.int32, "sorted_expert_ids"), (nv, 1, torch.int32, "num_valid")):
+        _dev(t, dt, name)
+        if not t.is_contiguous() or t.numel() < n:
+            raise ValueError("%s must be contiguous with at least %d entries" % (name, n))
+    _dev(workspace, torch.uint8, "workspace")
     ld = _rows(topk_ids, "topk_ids")
     if _rows(topk_weights, "topk_weights") != ld:
         raise ValueError("topk_ids and topk_weights must share a row stride")
@@ -166,9 +187,13 @@ def fp8_quant_1x128(x, q=None, scale=None, scale_layout="row"):
     KB = _nblk(K)
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    shape = (M, KB) if scale_layout == "row" else (KB, M)
     if scale is None:
-        shape = (M, KB) if scale_layout == "row" else (KB, M)
         scale = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _dev(q, torch.uint8, "q")
+    if tuple(q.shape) != (M, K):
+        raise ValueError("q must be [M, K] = %s, got %s" % ((M, K), tuple(q.shape)))
+    _need(scale, shape, torch.float32, "scale")
     ssm, sskb = (KB, 1) if scale_layout == "row" else (1, M)
     _check(lib().fp8_quant_1x128(_ptr(x), _rows(x, "x"), M, K, _ptr(q), _rows(q, "q"), _ptr(scale), ssm, sskb,
                                  _stream()))
@@ -181,11 +206,14 @@ def _nblk(n):
 
 
 def _scale_strides(a_scale, T, H, scale_layout):
+    """Element strides (per row, per K block) of 1x128 activation scales in either layout."""
     KB = _nblk(H)
     if scale_layout == "row":
-        assert a_scale.shape == (T, KB)
+        _need(a_scale, (T, KB), torch.float32, "a_scale")
         return KB, 1
-    assert a_scale.shape == (KB, T)
+    if scale_layout != "kblock":
+        raise ValueError("scale_layout must be 'row' or 'kblock'")
+    _need(a_scale, (KB, T), torch.float32, "a_scale")
     return 1, T
 
 
@@ -197,24 +225,32 @@ def moe_fp8_blockscale_g1u1(a8, a_scale, w1, w1_scale, sorted_ids, sorted_expert
     Returns (h8 [max_sorted, I], h_scale [max_sorted, I/128]).  preshuffled: w1 holds
     shuffle_weight_128x128 output (same shape).
     """
-    _dev(a8, torch.uint8, "a8")
-    _dev(w1, torch.uint8, "w1")
     T, H = a8.shape
     E, twoI, _ = w1.shape
     I = twoI // 2
+    _need(a8, (T, H), torch.uint8, "a8")
+    _need(w1, (E, 2 * I, H), torch.uint8, "w1")
+    _need(w1_scale, (E, _nblk(2 * I), _nblk(H)), torch.float32, "w1_scale")
     ms = sorted_ids.numel()
+    _need(sorted_ids, (ms,), torch.int32, "sorted_ids")
+    _need(sorted_expert_ids, (sorted_expert_ids.numel(),), torch.int32, "sorted_expert_ids")
+    if block_m <= 0 or sorted_expert_ids.numel() < ms // block_m:
+        raise ValueError("sorted_expert_ids must hold max_sorted / block_m entries")
+    _need(num_valid, (1,), torch.int32, "num_valid")
     if h8 is None:
         h8 = torch.empty((ms, I), dtype=torch.uint8, device=a8.device)
     if h_scale is None:
         h_scale = torch.empty((ms, I // 128), dtype=torch.float32, device=a8.device)
+    _need(h8, (ms, I), torch.uint8, "h8")
+    _need(h_scale, (ms, _nblk(I)), torch.float32, "h_scale")
+    if fc2_smooth_scale is not None:
+        _need(fc2_smooth_scale, (E, I), torch.float32, "fc2_smooth_scale")
     ssm, sskb = _scale_strides(a_scale, T, H, scale_layout)
     fn = lib().moe_fp8_blockscale_g1u1_wpreshuffle if preshuffled else lib().moe_fp8_blockscale_g1u1
     _check(fn(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(w1), _ptr(w1_scale),
               _ptr(sorted_ids), _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E,
               topk, block_m, ms, _ptr(h8), _ptr(h_scale),
-              _ptr(None if fc2_smooth_scale is None else
-                   _dev(fc2_smooth_scale, torch.float32, "fc2_smooth_scale").contiguous()),
-              _stream()))
+              _ptr(fc2_smooth_scale), _stream()))
     return h8, h_scale
 
 
@@ -228,14 +264,26 @@ def moe_down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sort
                      block_m, out=None, workspace=None, preshuffled=False):
     """Down grouped GEMM + top-k weighted combine.  Returns bf16 [T, H].  preshuffled: w2 holds
     shuffle_weight_128x128 output (same shape)."""
-    _dev(h8, torch.uint8, "h8")
-    _dev(w2, torch.uint8, "w2")
     E, H, I = w2.shape
+    _need(w2, (E, H, I), torch.uint8, "w2")
+    _need(w2_scale, (E, _nblk(H), _nblk(I)), torch.float32, "w2_scale")
     ms = sorted_ids.numel()
+    _need(sorted_ids, (ms,), torch.int32, "sorted_ids")
+    _need(sorted_weights, (ms,), torch.float32, "sorted_weights")
+    _need(sorted_expert_ids, (sorted_expert_ids.numel(),), torch.int32, "sorted_expert_ids")
+    if block_m <= 0 or sorted_expert_ids.numel() < ms // block_m:
+        raise ValueError("sorted_expert_ids must hold max_sorted / block_m entries")
+    _need(num_valid, (1,), torch.int32, "num_valid")
+    _need(h8, (ms, I), torch.uint8, "h8")
+    _need(h_scale, (ms, _nblk(I)), torch.float32, "h_scale")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=h8.device)
     if workspace is None:
         workspace = torch.empty(moe_down_combine_workspace(T, H, topk), dtype=torch.uint8, device=h8.device)
+    _dev(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (T, H):
+        raise ValueError("out must be [T, H] = %s, got %s" % ((T, H), tuple(out.shape)))
+    _dev(workspace, torch.uint8, "workspace")
     fn = lib().moe_down_combine_wpreshuffle if preshuffled else lib().moe_down_combine
     _check(fn(_ptr(h8), _ptr(h_scale), _ptr(w2), _ptr(w2_scale), _ptr(sorted_ids), _ptr(sorted_weights),
               _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E, topk, block_m, ms, _ptr(out), _rows(out, "out"),
@@ -275,18 +323,18 @@ def gemm_fp8_blockscale(a8, a_scale, b8, b_scale, c=None, scale_layout="row", wo
     workspace: None allocates what gemm_fp8_blockscale_workspace asks for; False runs
     without workspace (no split-K); or a device uint8 tensor.
     """
-    _dev(a8, torch.uint8, "a8")
-    _dev(b8, torch.uint8, "b8")
     M, K = a8.shape
     N = b8.shape[0]
-    if b8.shape[1] != K or b_scale.shape != (_nblk(N), _nblk(K)):
-        raise ValueError("b8 [N, K] with b_scale [ceil(N/128), ceil(K/128)] expected")
-    if not _dev(b_scale, torch.float32, "b_scale").is_contiguous():
-        raise ValueError("b_scale must be contiguous")
+    _need(a8, (M, K), torch.uint8, "a8")
+    _need(b8, (N, K), torch.uint8, "b8")
+    _need(b_scale, (_nblk(N), _nblk(K)), torch.float32, "b_scale")
     if c is None:
         c = torch.empty((M, N), dtype=out_dtype, device=a8.device)
     if c.dtype not in (torch.bfloat16, torch.float16):
         raise ValueError("c must be bf16 or fp16, got %s" % c.dtype)
+    _dev(c, c.dtype, "c")
+    if tuple(c.shape) != (M, N):
+        raise ValueError("c must be [M, N] = %s, got %s" % ((M, N), tuple(c.shape)))
     if workspace is None:
         n = gemm_fp8_blockscale_workspace(M, N, K)
         workspace = torch.empty(n, dtype=torch.uint8, device=a8.device) if n else False

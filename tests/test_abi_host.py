@@ -148,3 +148,14 @@ def test_block_m_table(lib):
     assert moe355.moe_block_m(0, 8, 256) == 16
     with pytest.raises(moe355.Moe355Error):
         moe355.moe_block_m(1, 0, 256)
+
+
+def test_binding_checks_run_on_the_host():
+    # the binding's tensor checks raise ValueError without touching a GPU: a host tensor
+    # where a device tensor is needed, an unknown scale layout
+    import torch
+    from fp8_block_scaled_grouped_amd import moe355
+    with pytest.raises(ValueError):
+        moe355._need(torch.zeros(4), (4,), torch.float32, "x")       # not a GPU tensor
+    with pytest.raises(ValueError):
+        moe355._scale_strides(torch.zeros((2, 2)), 2, 256, "columns")

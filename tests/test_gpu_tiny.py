@@ -370,6 +370,27 @@ def test_layer_graph_replay_matches_eager(m, tiny, BM):
         assert torch.equal(layer.out.view(torch.int16), eager.view(torch.int16)), "replay %d" % i
 
 
+def test_binding_rejects_wrong_shapes(m, tiny):
+    # a shape mistake raises in the binding before any pointer reaches a kernel
+    cfg, x = tiny
+    g = {k: v.to(DEV) for k, v in x.items()}
+    layer = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"])
+    layer.forward(g["hidden"], g["logits"])
+    sid, sw, seid, nv = layer.sort_out
+    with pytest.raises(ValueError):
+        m.moe_fp8_blockscale_g1u1(layer.a8, layer.a_scale, g["w1"], g["w1_scale"][:, :1].contiguous(), sid, seid, nv,
+                                  cfg.topk, layer.block_m, layer.h8, layer.h_scale)
+    with pytest.raises(ValueError):
+        m.moe_down_combine(layer.h8[:-1], layer.h_scale, g["w2"], g["w2_scale"], sid, sw, seid, nv, cfg.T, cfg.topk,
+                           layer.block_m)
+    with pytest.raises(ValueError):
+        m.gemm_fp8_blockscale(layer.a8, layer.a_scale, g["w2"][0], g["w2_scale"][0],
+                              c=torch.empty((cfg.T, 8), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        m.fp8_quant_1x128(g["hidden"], scale=torch.empty((cfg.T, 1), device=DEV))
+    torch.cuda.synchronize()
+
+
 def test_dense_split_deterministic(m):
     from fp8_block_scaled_grouped_amd import inputs
     M, N, K = 3, 2048, 7168
