@@ -458,3 +458,35 @@ def test_dense_fp16_output(m, M, N, K):
     assert_rel_max(c.float().cpu().numpy().astype(np.float64), ref, what="dense fp16 %dx%dx%d" % (M, N, K))
     # same fp32 result rounded two ways: fp16 and bf16 agree to bf16 precision
     assert torch.allclose(c.float(), cb.float(), rtol=2 ** -7, atol=1e-3)
+
+
+@pytest.mark.parametrize("seed", range(1, 9))
+def test_layer_seeds_all_stages(m, seed):
+    # the whole layer on fresh draws: routing, sort and quantised bytes bit-exact, h within the
+    # requantisation bar, output within 1e-2 max|ref|; a mid-sized shape (E 64 in 8 groups,
+    # top-6 of 3 groups, H 512, I 384) and an M tile drawn per seed
+    from fp8_block_scaled_grouped_amd import inputs
+    BM = [16, 32, 64, 128][seed % 4]
+    T = [7, 100, 333, 1024][seed % 4]
+    cfg = inputs.MoEConfig("seeds", T=T, H=512, I=384, E=64, n_group=8, topk_group=3, topk=6, block_m=BM)
+    print("seed", seed, "T", T, "BM", BM, flush=True)
+    x = inputs.make_moe_inputs(cfg, DEV, seed=seed)
+    layer = m.MoELayer(cfg, x["bias"], x["w1"], x["w1_scale"], x["w2"], x["w2_scale"])
+    out = layer.forward(x["hidden"], x["logits"])
+    torch.cuda.synchronize()
+    w, ids = oracle_routing(x, cfg)
+    assert np.array_equal(layer.topk_ids.cpu().numpy(), ids)
+    assert np.array_equal(layer.topk_w.cpu().numpy().view(np.uint32), w.view(np.uint32))
+    rsid, rsw, rseid, P = oracle.sort.moe_sort(ids, w, cfg.E, BM)
+    sid, sw, seid, nv = layer.sort_out
+    assert int(nv.item()) == P and np.array_equal(sid[:P].cpu().numpy(), rsid)
+    assert np.array_equal(seid[:P // BM].cpu().numpy(), rseid)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(x["hidden"]))
+    assert np.array_equal(np_u8(layer.a8), a8)
+    assert np.array_equal(layer.a_scale.cpu().numpy().view(np.uint32), sa.view(np.uint32))
+    ref, h_ref, _, _ = oracle.moe.layer_tokens(a8, sa, x["w1"].cpu().numpy(), x["w1_scale"].cpu().numpy(),
+                                               x["w2"].cpu().numpy(), x["w2_scale"].cpu().numpy(), ids, w)
+    assert_rel_max(f32_of_bf16(out), ref, what="seed %d layer" % seed)
+    pos = {int(p): r for r, p in enumerate(rsid) if p < T * cfg.topk}
+    rows = [pos[t * cfg.topk + j] for t in range(T) for j in range(cfg.topk)]
+    check_requant(np_u8(layer.h8)[rows], layer.h_scale.cpu().numpy()[rows], h_ref.reshape(-1, cfg.I))
