@@ -286,7 +286,7 @@ def bench_moe(a):
                                "topk_group %d, top-%d, block_m %d" % (a.workload, T, H, I, cfg.E, cfg.n_group,
                                                                       cfg.topk_group, k, bm),
                    "tokens": T, "hidden": H, "intermediate": I, "experts": cfg.E, "topk": k, "block_m": bm,
-                   "preshuffled_weights": bool(a.preshuffle)},
+                   "preshuffled_weights": bool(a.preshuffle), "seed": a.seed},
         "layer_tflops": flops / (ms * 1e-3) / 1e12, "layer_gbs": nbytes / (ms * 1e-3) / 1e9,
         "layer_frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
@@ -358,7 +358,7 @@ def bench_dense(a):
             "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic",
             "config": {"workload": "dense FP8 block-scale GEMM M=%d N=%d K=%d (quant + GEMM)" % (M, N, K),
                        "M": M, "N": N, "K": K, "weight_copies": ncopy, "split_k_workspace_bytes": nws,
-                       "preshuffled_weights": bool(a.preshuffle)},
+                       "preshuffled_weights": bool(a.preshuffle), "seed": a.seed},
             "roofline": roof}
 
 
