@@ -1,15 +1,24 @@
 """Benchmark of the FP8 block-scale MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skew|tiny|dense]
-                    [--block-m BM] [--dense-m M --dense-n N] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload prefill|decode|skew|tiny|dense|prefill_bias0|skew_zipf]
+                    [--tokens T] [--block-m BM] [--dense-m M --dense-n N] [--no-cpu-baseline]
+                    [--no-decode] [--sweep block_m|dense]
 
 A step is one pass of the whole layer -- grouped_topk, moe_sort,
 fp8_quant_1x128, moe_fp8_blockscale_g1u1, moe_down_combine -- over one batch
 of synthetic tokens whose inputs and weights are already resident in HBM.
 (`--workload dense` times fp8_quant_1x128 + gemm_fp8_blockscale instead.)
-Prints one JSON line.  The default workload is the 64-token decode layer
-of DeepSeek-V3 shape (hidden 7168, intermediate 2048, 256 experts in 8
-groups, topk_group 4, top-8).
+Prints one JSON line.  The default workload is the largest configuration:
+the 8192-token prefill layer of DeepSeek-V3 shape (hidden 7168,
+intermediate 2048, 256 experts in 8 groups, topk_group 4, top-8), with its
+roofline on the FP8 matrix cores; the 64-token decode layer on the same
+weights is reported beside it (object "decode", roofline on HBM).
+
+--sweep block_m times the whole layer for every M tile over a range of token
+counts (the table behind moe_block_m); --sweep dense times the dense GEMM on
+the linear-layer shapes of a DeepSeek-V3 layer.  Sweeps print one JSON line
+per measurement and no bench line.
 """
 import argparse
 import json
@@ -30,10 +39,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode",
+    ap.add_argument("--workload", default="prefill",
                     choices=["decode", "prefill", "skew", "tiny", "dense", "prefill_bias0", "skew_zipf"],
                     help="prefill_bias0 / skew_zipf: labelled routing controls (zero bias; Zipf without the hot bias)")
     ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--tokens", type=int, default=None, help="token count of a MoE workload (default: its own)")
+    ap.add_argument("--no-decode", action="store_true", help="prefill: leave out the decode layer beside it")
+    ap.add_argument("--sweep", choices=["block_m", "dense"], default=None)
     ap.add_argument("--graph", action="store_true",
                     help="also time the layer captured once as a HIP graph and replayed (graph_ms_per_step)")
     ap.add_argument("--preshuffle", action="store_true",
@@ -42,7 +54,6 @@ def parse():
     ap.add_argument("--dense-n", type=int, default=18432)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, copy BYTES bytes device-to-device 3 times (plain copy kernel whose "
                          "FETCH_SIZE / WRITE_SIZE calibrate the traffic counters)")
@@ -113,20 +124,36 @@ class _ExpertRows:
         return self.d[e]
 
 
-def cpu_baseline_moe(cfg, hidden, logits, bias, w1, s1, w2, s2, budget_s):
-    """Time the oracle on the host for as many tokens as fit in about budget_s seconds.
+def host_cpu():
+    """(cores this process may run on, CPU model name) of the host."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return n, model
 
-    The oracle runs as it stands: routing for all tokens, then token by token the
-    1x128 quantisation and the token-major expert evaluation.  Weight copies to the
-    host are made before the clock starts.
+
+def cpu_baseline_moe(cfg, hidden, logits, bias, w1, s1, w2, s2):
+    """The oracle as it stands, timed on the host cores on the whole layer: routing of all
+    T tokens, their 1x128 quantisation, and the expert-batched evaluation of every routed
+    pair (gate/up, SiLU*up, requantisation, down projection) with the weighted combine.
+
+    The oracle evaluates independent (expert, block of rows) pieces on its thread pool;
+    the host copies of the routed experts' weights are made before the clock starts.
     """
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    from oracle.pool import default_workers
+    workers = default_workers()
+    ncpu, model = host_cpu()
     hid = oracle.fp8.bf16_bits_to_f32(hidden.cpu().view(torch_int16()).numpy().view(np.uint16))
     logits = logits.cpu().numpy()
     bias = bias.cpu().numpy()
@@ -136,19 +163,16 @@ def cpu_baseline_moe(cfg, hidden, logits, bias, w1, s1, w2, s2, budget_s):
     w, ids = oracle.routing.grouped_topk(logits, bias, cfg.n_group, cfg.topk_group, cfg.topk, cfg.renorm,
                                          cfg.routed_scaling_factor)
     t_route = time.perf_counter() - t0
-    done, el = 0, 0.0
-    while done < cfg.T and el < budget_s:
-        for e in ids[done]:                       # host copies outside the clock
-            W1[e], W2[e]
-        t0 = time.perf_counter()
-        a8, sa = oracle.quant.quant_1x128(hid[done:done + 1])
-        oracle.moe.layer_tokens(a8, sa, W1, s1, W2, s2, ids[done:done + 1], w[done:done + 1])
-        el += time.perf_counter() - t0
-        done += 1
-    sec = el + t_route * done / cfg.T
-    return {"value": done / sec, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d of %d tokens through the whole layer (routing of all %d tokens charged pro rata), "
-                      "%.1f s" % (done, cfg.T, cfg.T, sec)}
+    for e in np.unique(ids):                      # host copies outside the clock
+        W1[e], W2[e]
+    t0 = time.perf_counter()
+    a8, sa = oracle.quant.quant_1x128(hid, workers=workers)
+    oracle.moe.layer_tokens(a8, sa, W1, s1, W2, s2, ids, w, workers=workers)
+    sec = t_route + time.perf_counter() - t0
+    return {"value": cfg.T / sec, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": "all %d of %d tokens through the whole layer (routing, quantisation, every routed pair's "
+                      "expert GEMMs and the combine), %.1f s" % (cfg.T, cfg.T, sec),
+            "host_cores_available": ncpu, "cpu_model": model, "seconds": sec}
 
 
 def torch_int16():
@@ -156,38 +180,47 @@ def torch_int16():
     return torch.int16
 
 
-def bench_moe(a):
-    import numpy as np
+def moe_config(workload, tokens=None):
+    from fp8_block_scaled_grouped_amd import inputs
+    cfg = {**inputs.MOE_CONFIGS, **inputs.CONTROL_CONFIGS}[workload]
+    return inputs.with_tokens(cfg, tokens) if tokens else cfg
+
+
+def moe_inputs(cfg, seed, weights=None):
+    """Device inputs of a MoE workload; the expert weights are generated unless given."""
+    import torch
+    from fp8_block_scaled_grouped_amd import inputs
+    dev = torch.device("cuda:0")
+    x = inputs.make_moe_inputs(cfg, "cpu" if cfg.name == "tiny" else dev, seed=seed, weights=weights is None)
+    x = {k: v.to(dev) for k, v in x.items()}
+    if weights is not None:
+        x.update(weights)
+    torch.cuda.synchronize()
+    return x
+
+
+def time_layer(cfg, x, bm, steps, warmup, preshuffle=False, graph=False, per_call=True):
+    """Time K whole layer steps on the current stream; the g1u1 launch of every step is
+    bracketed by events on the same stream.  Returns a dict of timings and the layer."""
     import torch
 
     import fp8_block_scaled_grouped_amd as m
-    from fp8_block_scaled_grouped_amd import inputs
 
-    cfg = {**inputs.MOE_CONFIGS, **inputs.CONTROL_CONFIGS}[a.workload]
-    bm = a.block_m or cfg.block_m
-    dev = torch.device("cuda:0")
-    t0 = time.time()
-    x = inputs.make_moe_inputs(cfg, "cpu" if a.workload == "tiny" else dev, seed=a.seed)
-    x = {k: v.to(dev) for k, v in x.items()}
-    torch.cuda.synchronize()
-    gen_s = time.time() - t0
     layer = m.MoELayer(cfg, x["bias"], x["w1"], x["w1_scale"], x["w2"], x["w2_scale"], block_m=bm,
-                       preshuffle=a.preshuffle)
+                       preshuffle=preshuffle)
     hidden, logits = x["hidden"], x["logits"]
-
     stream = torch.cuda.current_stream()
-    for _ in range(a.warmup):
+    for _ in range(warmup):
         layer.forward(hidden, logits)
     torch.cuda.synchronize()
 
-    # timed region: K whole steps; the dominant kernel (g1u1) bracketed by events inside it
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    st = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]  # start of each step
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c = cfg
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]  # start of each step
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(a.steps):
+    for i in range(steps):
         st[i].record(stream)
         m.grouped_topk(logits, layer.bias, c.n_group, c.topk_group, c.topk, c.renorm, c.routed_scaling_factor,
                        layer.topk_w, layer.topk_ids)
@@ -201,60 +234,72 @@ def bench_moe(a):
                            bm, layer.out, layer.down_ws, preshuffled=layer.preshuffle)
     end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / a.steps
-    g1u1_ms = sum(s.elapsed_time(e) for s, e in ev) / a.steps
-    steps_ms = sorted([st[i].elapsed_time(st[i + 1]) for i in range(a.steps - 1)] + [st[-1].elapsed_time(end)])
-    layer_stats = {"median_ms": steps_ms[len(steps_ms) // 2], "min_ms": steps_ms[0]}
+    ms = start.elapsed_time(end) / steps
+    g1u1_ms = sum(s.elapsed_time(e) for s, e in ev) / steps
+    steps_ms = sorted([st[i].elapsed_time(st[i + 1]) for i in range(steps - 1)] + [st[-1].elapsed_time(end)])
+    r = {"ms": ms, "g1u1_ms": g1u1_ms, "layer": layer, "sid": sid, "sw": sw, "seid": seid, "nv": nv,
+         "layer_ms": {"median_ms": steps_ms[len(steps_ms) // 2], "min_ms": steps_ms[0]}}
 
-    graph = None
-    if a.graph:
+    if graph:
         # the five calls captured once into a HIP graph (the library allocates nothing and
         # never synchronises, so the layer is capturable) and replayed K times
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             layer.forward(hidden, logits)
-        for _ in range(a.warmup):
+        for _ in range(warmup):
             g.replay()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         g0.record(stream)
-        for _ in range(a.steps):
+        for _ in range(steps):
             g.replay()
         g1.record(stream)
         torch.cuda.synchronize()
-        graph = g0.elapsed_time(g1) / a.steps
+        r["graph_ms"] = g0.elapsed_time(g1) / steps
         del g
 
-    # per-call breakdown (outside the timed region): events around each of the five calls
-    calls = [
-        ("grouped_topk", lambda: m.grouped_topk(logits, layer.bias, c.n_group, c.topk_group, c.topk, c.renorm,
-                                                c.routed_scaling_factor, layer.topk_w, layer.topk_ids)),
-        ("moe_sort", lambda: m.moe_sort(layer.topk_ids, layer.topk_w, c.E, bm, layer.sort_out, layer.sort_ws)),
-        ("fp8_quant_1x128", lambda: m.fp8_quant_1x128(hidden, layer.a8, layer.a_scale)),
-        ("moe_fp8_blockscale_g1u1", lambda: m.moe_fp8_blockscale_g1u1(layer.a8, layer.a_scale, layer.w1,
-                                                                      layer.w1_scale, sid, seid, nv, c.topk, bm,
-                                                                      layer.h8, layer.h_scale,
-                                                                      preshuffled=layer.preshuffle)),
-        ("moe_down_combine", lambda: m.moe_down_combine(layer.h8, layer.h_scale, layer.w2, layer.w2_scale, sid, sw,
-                                                        seid, nv, layer.T, c.topk, bm, layer.out,
-                                                        layer.down_ws, preshuffled=layer.preshuffle)),
-    ]
-    reps = max(10, a.steps)
-    cev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-           for _ in range(reps)]
-    for r in range(reps):
-        for (name, fn), (e0, e1) in zip(calls, cev[r]):
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-    torch.cuda.synchronize()
-    per_call = {}
-    for ci, (name, _) in enumerate(calls):
-        t = sorted(cev[r][ci][0].elapsed_time(cev[r][ci][1]) for r in range(reps))
-        per_call[name] = {"median_ms": t[len(t) // 2], "min_ms": t[0]}
+    if per_call:
+        # per-call breakdown (outside the timed region): events around each of the five calls
+        calls = [
+            ("grouped_topk", lambda: m.grouped_topk(logits, layer.bias, c.n_group, c.topk_group, c.topk, c.renorm,
+                                                    c.routed_scaling_factor, layer.topk_w, layer.topk_ids)),
+            ("moe_sort", lambda: m.moe_sort(layer.topk_ids, layer.topk_w, c.E, bm, layer.sort_out, layer.sort_ws)),
+            ("fp8_quant_1x128", lambda: m.fp8_quant_1x128(hidden, layer.a8, layer.a_scale)),
+            ("moe_fp8_blockscale_g1u1", lambda: m.moe_fp8_blockscale_g1u1(layer.a8, layer.a_scale, layer.w1,
+                                                                          layer.w1_scale, sid, seid, nv, c.topk, bm,
+                                                                          layer.h8, layer.h_scale,
+                                                                          preshuffled=layer.preshuffle)),
+            ("moe_down_combine", lambda: m.moe_down_combine(layer.h8, layer.h_scale, layer.w2, layer.w2_scale, sid,
+                                                            sw, seid, nv, layer.T, c.topk, bm, layer.out,
+                                                            layer.down_ws, preshuffled=layer.preshuffle)),
+        ]
+        reps = max(10, steps)
+        cev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+               for _ in range(reps)]
+        for rr in range(reps):
+            for (name, fn), (e0, e1) in zip(calls, cev[rr]):
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+        torch.cuda.synchronize()
+        pc = {}
+        for ci, (name, _) in enumerate(calls):
+            t = sorted(cev[rr][ci][0].elapsed_time(cev[rr][ci][1]) for rr in range(reps))
+            pc[name] = {"median_ms": t[len(t) // 2], "min_ms": t[0]}
+        r["per_call_ms"] = pc
+    return r
 
+
+def moe_report(cfg, bm, tm, workload, seed, preshuffle):
+    """Bench-line fields of one timed MoE workload: tokens/s, layer TFLOP/s and GB/s, the
+    routing statistics and the roofline of the dominant kernel (moe_fp8_blockscale_g1u1)."""
+    import torch
+    from fp8_block_scaled_grouped_amd import inputs
+
+    layer = tm["layer"]
+    ms, g1u1_ms = tm["ms"], tm["g1u1_ms"]
     ids = layer.topk_ids.cpu().numpy()
-    hot = inputs.hot_expert_mask(cfg, dev, a.seed).cpu().numpy() if cfg.skew else None
+    hot = inputs.hot_expert_mask(cfg, torch.device("cuda:0"), seed).cpu().numpy() if cfg.skew else None
     rs = routing_stats(ids, cfg.E, bm, hot)
     n_active = rs["active_experts"]
     flops = inputs.moe_flops(cfg)
@@ -266,8 +311,7 @@ def bench_moe(a):
     g1u1_bytes = (n_active * per_expert_w1 + T * H + 4 * T * (H // 128) + 4 * layer.max_sorted
                   + T * k * (I + 4 * (I // 128)))
     g1u1_flops = 2.0 * T * k * 2 * I * H
-    hbm_bound = cfg.T <= 512
-    if hbm_bound:
+    if cfg.T <= 512:
         roof = {"bound": "hbm", "achieved": g1u1_bytes / (g1u1_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     else:
@@ -276,90 +320,167 @@ def bench_moe(a):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = "moe_fp8_blockscale_g1u1"
     roof["kernel_ms"] = g1u1_ms
-    roof["traffic"] = measured_traffic(a.workload, "g1u1")
-
+    roof["algorithmic_per_launch"] = g1u1_bytes if roof["bound"] == "hbm" else g1u1_flops
+    roof["traffic"] = measured_traffic(workload, "g1u1")
     res = {
-        "metric": "FP8 blockscale MoE layer tokens/s", "value": T / (ms * 1e-3), "unit": "tokens/s",
-        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic",
+        "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
         "config": {"workload": "%s MoE layer: %d tokens, hidden %d, intermediate %d, %d experts / %d groups, "
-                               "topk_group %d, top-%d, block_m %d" % (a.workload, T, H, I, cfg.E, cfg.n_group,
+                               "topk_group %d, top-%d, block_m %d" % (workload, T, H, I, cfg.E, cfg.n_group,
                                                                       cfg.topk_group, k, bm),
                    "tokens": T, "hidden": H, "intermediate": I, "experts": cfg.E, "topk": k, "block_m": bm,
-                   "preshuffled_weights": bool(a.preshuffle), "seed": a.seed},
+                   "preshuffled_weights": bool(preshuffle), "seed": seed},
         "layer_tflops": flops / (ms * 1e-3) / 1e12, "layer_gbs": nbytes / (ms * 1e-3) / 1e9,
         "layer_frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
-        "routing": rs, "roofline": roof, "layer_ms": layer_stats, "per_call_ms": per_call,
-        "input_gen_s": round(gen_s, 2),
+        "routing": rs, "roofline": roof, "layer_ms": tm["layer_ms"],
     }
-    if graph is not None:
-        res["graph_ms_per_step"] = graph
-        res["graph_tokens_per_s"] = T / (graph * 1e-3)
-    if not a.no_cpu_baseline:
-        # the oracle reads the weights as loaded (row-major), not the layer's shuffled copies
-        res["cpu_baseline"] = cpu_baseline_moe(cfg, hidden, logits, layer.bias, x["w1"], layer.w1_scale, x["w2"],
-                                               layer.w2_scale, a.cpu_seconds)
+    if "per_call_ms" in tm:
+        res["per_call_ms"] = tm["per_call_ms"]
+    if "graph_ms" in tm:
+        res["graph_ms_per_step"] = tm["graph_ms"]
+        res["graph_tokens_per_s"] = T / (tm["graph_ms"] * 1e-3)
     return res
 
 
-def bench_dense(a):
+def bench_moe(a):
+    cfg = moe_config(a.workload, a.tokens)
+    bm = a.block_m or cfg.block_m
+    t0 = time.time()
+    x = moe_inputs(cfg, a.seed)
+    gen_s = time.time() - t0
+    tm = time_layer(cfg, x, bm, a.steps, a.warmup, a.preshuffle, a.graph)
+    rep = moe_report(cfg, bm, tm, a.workload, a.seed, a.preshuffle)
+    res = {"metric": "FP8 blockscale MoE layer tokens/s", "value": rep.pop("tokens_per_s"), "unit": "tokens/s",
+           "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": rep.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)",
+           "data": "synthetic"}
+    res.update(rep)
+    res["input_gen_s"] = round(gen_s, 2)
+    del tm
+    if a.workload == "prefill" and not a.no_decode and not a.tokens:
+        # the 64-token decode layer on the same expert weights: the HBM-bound configuration
+        dcfg = moe_config("decode")
+        w = {k: x[k] for k in ("w1", "w1_scale", "w2", "w2_scale")}
+        dx = moe_inputs(dcfg, a.seed, weights=w)
+        dtm = time_layer(dcfg, dx, dcfg.block_m, max(a.steps, 20), a.warmup, a.preshuffle, per_call=True)
+        res["decode"] = moe_report(dcfg, dcfg.block_m, dtm, "decode", a.seed, a.preshuffle)
+        del dtm
+    if not a.no_cpu_baseline:
+        # the oracle reads the weights as loaded (row-major), not shuffled copies
+        layer_scales = (x["w1_scale"], x["w2_scale"])
+        res["cpu_baseline"] = cpu_baseline_moe(cfg, x["hidden"], x["logits"], x["bias"], x["w1"], layer_scales[0],
+                                               x["w2"], layer_scales[1])
+    return res
+
+
+def sweep_block_m(a):
+    """Whole-layer time for every M tile over token counts (prefill routing distribution)."""
+    base = moe_config("prefill")
+    w = None
+    for T in (a.tokens,) if a.tokens else (1, 16, 64, 256, 1024, 4096, 8192):
+        cfg = moe_config("prefill", T)
+        x = moe_inputs(cfg, a.seed, weights=w)
+        w = {k: x[k] for k in ("w1", "w1_scale", "w2", "w2_scale")}
+        for bm in (16, 32, 64, 128):
+            tm = time_layer(cfg, x, bm, a.steps, a.warmup, a.preshuffle, per_call=False)
+            print(json.dumps({"sweep": "block_m", "tokens": T, "block_m": bm, "ms": tm["ms"],
+                              "median_ms": tm["layer_ms"]["median_ms"], "g1u1_ms": tm["g1u1_ms"],
+                              "hidden": base.H, "intermediate": base.I, "experts": base.E, "topk": base.topk}),
+                  flush=True)
+            del tm
+
+
+# (N, K) of the linear layers of a DeepSeek-V3 layer
+V3_LINEAR = [("q_a_proj", 1536, 7168), ("kv_a_proj", 576, 7168), ("q_b_proj", 24576, 1536),
+             ("kv_b_proj", 32768, 512), ("o_proj", 7168, 16384), ("dense_mlp_gate_up", 36864, 7168),
+             ("dense_mlp_down", 7168, 18432), ("shared_gate_up", 4096, 7168), ("shared_down", 7168, 2048),
+             ("config_n2048", 2048, 7168), ("config_n18432", 18432, 7168)]
+
+
+def time_dense(M, N, K, steps, warmup, seed=0, preshuffle=False):
+    """quant + GEMM per step, and the GEMM call alone back to back, over rotated weight copies."""
     import torch
 
     import fp8_block_scaled_grouped_amd as m
     from fp8_block_scaled_grouped_amd import inputs
 
-    M, N, K = a.dense_m, a.dense_n, inputs.DENSE_K
     dev = torch.device("cuda:0")
-    d = inputs.make_dense_inputs(M, N, K, dev, seed=a.seed)
+    d = inputs.make_dense_inputs(M, N, K, dev, seed=seed)
     # rotate distinct weight copies so a small B is not served from the 256 MB MALL
     ncopy = max(1, min(48, (8 << 30) // (N * K)))  # >= 40 copies below 200 MB of weights
     bs = [d["b"]] + [d["b"].clone() for _ in range(ncopy - 1)]
-    if a.preshuffle:
+    if preshuffle:
         bs = [m.shuffle_weight_128x128(b) for b in bs]
     a8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    sa = torch.empty((M, -(-K // 128)), dtype=torch.float32, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     nws = m.gemm_fp8_blockscale_workspace(M, N, K)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else False
-    for i in range(a.warmup):
+    for i in range(warmup):
         m.fp8_quant_1x128(d["a"], a8, sa)
-        m.gemm_fp8_blockscale(a8, sa, bs[i % ncopy], d["b_scale"], c, workspace=ws, preshuffled=a.preshuffle)
+        m.gemm_fp8_blockscale(a8, sa, bs[i % ncopy], d["b_scale"], c, workspace=ws, preshuffled=preshuffle)
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(a.steps):
+    for i in range(steps):
         m.fp8_quant_1x128(d["a"], a8, sa)
-        m.gemm_fp8_blockscale(a8, sa, bs[i % ncopy], d["b_scale"], c, workspace=ws, preshuffled=a.preshuffle)
+        m.gemm_fp8_blockscale(a8, sa, bs[i % ncopy], d["b_scale"], c, workspace=ws, preshuffled=preshuffle)
     end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / a.steps
+    ms = start.elapsed_time(end) / steps
     # the GEMM call alone (with its split-K reduce), K launches back to back on the same stream:
     # events around every microsecond-scale launch would mostly time the events
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     g0.record(stream)
-    for i in range(a.steps):
-        m.gemm_fp8_blockscale(a8, sa, bs[(i + 1) % ncopy], d["b_scale"], c, workspace=ws, preshuffled=a.preshuffle)
+    for i in range(steps):
+        m.gemm_fp8_blockscale(a8, sa, bs[(i + 1) % ncopy], d["b_scale"], c, workspace=ws, preshuffled=preshuffle)
     g1.record(stream)
     torch.cuda.synchronize()
-    gms = g0.elapsed_time(g1) / a.steps
+    gms = g0.elapsed_time(g1) / steps
     flops = 2.0 * M * N * K
-    gbytes = N * K + 4 * (N // 128) * (K // 128) + M * K + 4 * M * (K // 128) + 2 * M * N
+    nb, kb = -(-N // 128), -(-K // 128)
+    gbytes = N * K + 4 * nb * kb + M * K + 4 * M * kb + 2 * M * N
+    del bs, d
+    return {"ms": ms, "gemm_ms": gms, "flops": flops, "bytes": gbytes, "copies": ncopy, "workspace": nws}
+
+
+def dense_roof(M, t):
     if M <= 64:
-        roof = {"bound": "hbm", "achieved": gbytes / (gms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": t["bytes"] / (t["gemm_ms"] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops / (gms * 1e-3) / 1e12, "peak": FP8_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "achieved": t["flops"] / (t["gemm_ms"] * 1e-3) / 1e12, "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
-    roof.update(frac=roof["achieved"] / roof["peak"], kernel="gemm_fp8_blockscale", kernel_ms=gms,
-                traffic=measured_traffic("dense_%d_%d" % (M, N), "dense"))
-    return {"metric": "FP8 blockscale dense GEMM TFLOP/s", "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
-            "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)", "data": "synthetic",
+    roof.update(frac=roof["achieved"] / roof["peak"], kernel="gemm_fp8_blockscale", kernel_ms=t["gemm_ms"])
+    return roof
+
+
+def bench_dense(a):
+    from fp8_block_scaled_grouped_amd import inputs
+    M, N, K = a.dense_m, a.dense_n, inputs.DENSE_K
+    t = time_dense(M, N, K, a.steps, a.warmup, a.seed, a.preshuffle)
+    roof = dense_roof(M, t)
+    roof["traffic"] = measured_traffic("dense_%d_%d" % (M, N), "dense")
+    return {"metric": "FP8 blockscale dense GEMM TFLOP/s", "value": t["flops"] / (t["ms"] * 1e-3) / 1e12,
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": t["ms"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)",
+            "data": "synthetic",
             "config": {"workload": "dense FP8 block-scale GEMM M=%d N=%d K=%d (quant + GEMM)" % (M, N, K),
-                       "M": M, "N": N, "K": K, "weight_copies": ncopy, "split_k_workspace_bytes": nws,
-                       "preshuffled_weights": bool(a.preshuffle), "seed": a.seed},
+                       "M": M, "N": N, "K": K, "weight_copies": t["copies"], "split_k_workspace_bytes":
+                       t["workspace"], "preshuffled_weights": bool(a.preshuffle), "seed": a.seed},
             "roofline": roof}
+
+
+def sweep_dense(a):
+    """The dense GEMM on every linear-layer shape of a DeepSeek-V3 layer at M 1, 64, 4096."""
+    for name, N, K in V3_LINEAR:
+        for M in (a.dense_m,) if a.tokens else (1, 64, 4096):
+            t = time_dense(M, N, K, a.steps, a.warmup, a.seed, a.preshuffle)
+            r = dense_roof(M, t)
+            print(json.dumps({"sweep": "dense", "layer": name, "M": M, "N": N, "K": K, "gemm_us": t["gemm_ms"] * 1e3,
+                              "bound": r["bound"], "achieved": r["achieved"], "unit": r["unit"], "frac": r["frac"]}),
+                  flush=True)
 
 
 def main():
@@ -368,6 +489,12 @@ def main():
         print("bench.py: libmoe355 runs the layer on one GPU (it is not sharded across GPUs); "
               "run without --gpus or with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if a.sweep == "block_m":
+        sweep_block_m(a)
+        return
+    if a.sweep == "dense":
+        sweep_dense(a)
+        return
     res = bench_dense(a) if a.workload == "dense" else bench_moe(a)
     if a.copy_calibration:
         copy_calibration(a.copy_calibration)

@@ -760,6 +760,8 @@ int dense_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64
   MOE355_CHECK((int64_t)M * K < (1ll << 32) && (int64_t)N * K < (1ll << 32), MOE355_EUNSUPPORTED);
   if (M == 0 || N == 0) return MOE355_OK;
   MOE355_CHECK(K > 0 && a8 && a_scale && b8 && b_scale && c && sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
+  // the A-scale DMA takes a 32-bit byte offset per row: row * sstride_m * 4
+  MOE355_CHECK((int64_t)M * sstride_m * 4 < (1ll << 32), MOE355_EUNSUPPORTED);
   MOE355_CHECK(aligned16(a8) && aligned16(b8) && aligned16(c) && ldc % 8 == 0, MOE355_EMISALIGNED);
   MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0, MOE355_EMISALIGNED);
   DensePlan plan = dense_plan(M, N, K);
@@ -822,6 +824,8 @@ int g1u1_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_
   MOE355_CHECK(a8 && a_scale && w1 && w1_scale && sorted_ids && sorted_expert_ids && num_valid && h8 && h_scale,
                MOE355_EINVAL);
   MOE355_CHECK(sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
+  // the A-scale DMA takes a 32-bit byte offset per token row: t * sstride_m * 4
+  MOE355_CHECK((int64_t)T * sstride_m * 4 < (1ll << 32), MOE355_EUNSUPPORTED);
   MOE355_CHECK(aligned16(a8) && aligned16(w1) && aligned16(h8), MOE355_EMISALIGNED);
   MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0 && aligned16(fc2_smooth_scale),
                MOE355_EMISALIGNED);

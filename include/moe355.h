@@ -156,6 +156,7 @@ int fp8_quant_1x128(const uint16_t* x, int64_t ld_x, int M, int K,
  *           Padding rows and rows at or beyond num_valid are not written (nothing
  *           is written when num_valid is -1).
  * H % 128 == 0, I % 128 == 0, block_m in {16, 32, 64, 128}; a8, w1, h8 16-byte aligned.
+ * T * sstride_m * 4 < 2^32 (the scale reads take 32-bit byte offsets), else MOE355_EUNSUPPORTED.
  */
 int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale,
                             int64_t sstride_m, int64_t sstride_kb,
@@ -213,7 +214,8 @@ int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes);
  *          tile walks all of K.  Contents need no initialisation.  K above 16384 (more
  *          than 128 K blocks) is always split and needs the workspace: without it
  *          MOE355_EUNSUPPORTED, with too little MOE355_EINVAL.
- * K % 16 == 0, N % 8 == 0 (else MOE355_EUNSUPPORTED); a8, b8 16-byte aligned.
+ * K % 16 == 0, N % 8 == 0 and M * sstride_m * 4 < 2^32 (else MOE355_EUNSUPPORTED);
+ * a8, b8 16-byte aligned.
  */
 int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale,
                         int64_t sstride_m, int64_t sstride_kb,

@@ -24,5 +24,6 @@ gemm     block-scaled FP8 GEMM (exact 128-term block sums, binary64)
 moe      gate/up + SiLU*up + requantisation, down projection + combine,
          and a token-major evaluation of the whole layer
 layout   the pre-shuffled 128x128-tile weight layout (a byte permutation)
+pool     runs independent pieces (experts, blocks of rows) on host threads
 """
-from . import fp8, quant, routing, sort, gemm, moe, layout  # noqa: F401
+from . import fp8, pool, quant, routing, sort, gemm, moe, layout  # noqa: F401

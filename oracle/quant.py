@@ -16,15 +16,26 @@ K mod 128 values (ceil(K/128) scales per row, as the pages size them).
 """
 import numpy as np
 
-from . import fp8
+from . import fp8, pool
 
 GROUP = 128
 
 
-def quant_1x128(x):
-    """x: float32 [M, K] -> (q uint8 [M, K], scale float32 [M, ceil(K/128)])."""
+def quant_1x128(x, workers=1):
+    """x: float32 [M, K] -> (q uint8 [M, K], scale float32 [M, ceil(K/128)]).
+
+    workers > 1 quantises blocks of rows on a thread pool (rows are independent)."""
     x = np.asarray(x, dtype=np.float32)
     M, K = x.shape
+    if workers > 1 and M > 256:
+        q = np.zeros((M, K), dtype=np.uint8)
+        scale = np.ones((M, -(-K // GROUP)), dtype=np.float32)
+
+        def rows(r0, r1):
+            q[r0:r1], scale[r0:r1] = quant_1x128(x[r0:r1])
+
+        pool.run([lambda a=a, b=b: rows(a, b) for a, b in pool.row_chunks(M, 256)], workers)
+        return q, scale
     KB = -(-K // GROUP)
     q = np.zeros((M, K), dtype=np.uint8)
     scale = np.ones((M, KB), dtype=np.float32)

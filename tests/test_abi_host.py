@@ -99,6 +99,15 @@ def test_invalid_arguments_return_codes(lib):
     # pre-shuffled dense weights need whole 128x128 tiles
     assert L.gemm_fp8_blockscale_wpreshuffle(_p(), _p(), 2, 1, _p(), _p(), 4, 136, 256, _p(), 136, 0, None, 0,
                                              None) == -2
+    # A-scale row strides whose byte offset of the last row reaches 2^32 -> EUNSUPPORTED
+    # (the scale DMA takes a 32-bit offset per row): dense M 4096 with sstride_m 2^18,
+    # g1u1 T 16 with sstride_m 2^26; one element less is accepted as far as the checks go
+    assert L.gemm_fp8_blockscale(_p(), _p(), 1 << 18, 1, _p(), _p(), 4096, 128, 256, _p(), 128, 0, None, 0,
+                                 None) == -2
+    assert L.moe_fp8_blockscale_g1u1(_p(), _p(), 1 << 26, 1, _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16,
+                                     304, _p(), _p(), None, None) == -2
+    assert L.moe_fp8_blockscale_g1u1(_p(), _p(), 1 << 26, 1, _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16,
+                                     304, _p(8), _p(), None, None) == -2
     # down: workspace too small
     assert L.moe_down_combine(_p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16, 304, _p(),
                               256, _p(), 8, None) == -1

@@ -101,3 +101,19 @@ def test_encode_decode_roundtrip_all_finite_codes():
     d = fp8.decode(c)
     fin = ~np.isnan(d)
     assert np.array_equal(fp8.encode(d[fin].astype(np.float32)), c[fin])
+
+
+def test_bf16_widening_matches_torch_cast_all_patterns():
+    # every bf16 bit pattern widened by the oracle equals torch's bfloat16 -> float32 cast
+    # (a library routine): same value, same sign of zero, NaN exactly where torch has NaN
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = fp8.bf16_bits_to_f32(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float32).numpy()
+    assert got.dtype == np.float32
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    # a few values fixed by the format: 0x3F80 = 1, 0xC000 = -2, 0x7F80 = +inf, 0x0001 = 2^-133
+    spot = fp8.bf16_bits_to_f32(np.array([0x3F80, 0xC000, 0x7F80, 0x0001, 0x8000], np.uint16))
+    assert spot[0] == 1.0 and spot[1] == -2.0 and np.isposinf(spot[2]) and spot[3] == 2.0 ** -133
+    assert spot[4] == 0.0 and np.signbit(spot[4])

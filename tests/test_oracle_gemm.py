@@ -75,3 +75,16 @@ def test_partial_blocks_equal_zero_padded_problem(rng):
     full = gemm.gemm_blockscale(ap, sa, bp, sb)
     assert np.array_equal(out, full[:, :N])
     assert np.array_equal(gemm.block_sums(a, b), gemm.block_sums(ap, bp)[:, :, :N])
+
+
+def test_column_blocked_reference_equals_one_call():
+    # the parity tests evaluate large dense products in column blocks on a thread pool;
+    # every element must equal the single oracle call bit for bit
+    from tests.helpers import dense_ref
+    rng = np.random.default_rng(5)
+    a8 = rng.integers(0, 0x7E, (7, 400), dtype=np.uint8)
+    sa = rng.random((7, 4), dtype=np.float32)
+    b8 = rng.integers(0, 0x7E, (600, 400), dtype=np.uint8)
+    sb = rng.random((5, 4), dtype=np.float32)
+    one = gemm.gemm_blockscale(a8, sa, b8, sb)
+    assert np.array_equal(dense_ref(a8, sa, b8, sb, workers=3, cols=256), one)

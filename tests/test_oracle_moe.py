@@ -116,3 +116,32 @@ def test_smoothing_zero_channel_zeroes_its_codes(rng):
     _, _, hraw, _ = moe.g1u1(a8, sa, w1, s1, sid, seid, P, 1, 16)
     keep = np.arange(I) != 7
     assert np.array_equal(h[np.ix_(rows, keep)], hraw[np.ix_(rows, keep)])
+
+
+def test_worker_pool_gives_identical_results(rng):
+    # the thread-pool evaluation of independent experts / blocks / row groups equals the
+    # serial one bit for bit (block sums are exact, every piece writes its own rows)
+    from oracle import moe as omoe
+    a8, sa, w1, s1, w2, s2, w, ids = _small_layer(rng, T=40, E=4, k=2)
+    T, k = ids.shape
+    old = omoe.ROW_CHUNK
+    try:
+        omoe.ROW_CHUNK = 7                       # several pieces per expert
+        r1 = moe.layer_tokens(a8, sa, w1, s1, w2, s2, ids, w)
+        r4 = moe.layer_tokens(a8, sa, w1, s1, w2, s2, ids, w, workers=4)
+    finally:
+        omoe.ROW_CHUNK = old
+    for x1, x4 in zip(r1, r4):
+        assert np.array_equal(x1, x4)
+    sid, sw, seid, P = sort.moe_sort(ids, w, w1.shape[0], 16)
+    g1 = moe.g1u1(a8, sa, w1, s1, sid, seid, P, k, 16)
+    g4 = moe.g1u1(a8, sa, w1, s1, sid, seid, P, k, 16, workers=4)
+    for x1, x4 in zip(g1, g4):
+        assert np.array_equal(x1, x4)
+    d1 = moe.down_combine(g1[0], g1[1], w2, s2, sid, sw, seid, P, T, k, 16)
+    d4 = moe.down_combine(g1[0], g1[1], w2, s2, sid, sw, seid, P, T, k, 16, workers=4)
+    assert np.array_equal(d1, d4)
+    x = rng.standard_normal((700, 384)).astype(np.float32)
+    q1, s_1 = quant.quant_1x128(x)
+    q4, s_4 = quant.quant_1x128(x, workers=4)
+    assert np.array_equal(q1, q4) and np.array_equal(s_1, s_4)
