@@ -415,7 +415,7 @@ def time_dense(M, N, K, steps, warmup, seed=0, preshuffle=False):
     sa = torch.empty((M, -(-K // 128)), dtype=torch.float32, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     nws = m.gemm_fp8_blockscale_workspace(M, N, K)
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else False
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev) if nws else False
     for i in range(warmup):
         m.fp8_quant_1x128(d["a"], a8, sa)
         m.gemm_fp8_blockscale(a8, sa, bs[i % ncopy], d["b_scale"], c, workspace=ws, preshuffled=preshuffle)

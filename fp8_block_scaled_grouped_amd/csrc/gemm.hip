@@ -34,37 +34,11 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "gemm_engine.h"
 #include "host_common.h"
 
 namespace moe355 {
 namespace {
-
-enum Mode : int { kDense = 0, kG1U1 = 1, kDown = 2 };
-
-struct GemmArgs {
-  const uint8_t* a;        // dense: [M, K]; g1u1: a8 [T, K]; down: h8 [max_sorted, K]
-  const float* a_scale;    // element (row, kb) at a_scale[row * ssm + kb * sskb]
-  int64_t ssm, sskb;
-  const uint8_t* b;        // dense: [N, K]; g1u1: w1 [E, 2I, K]; down: w2 [E, N, K]
-  const float* b_scale;    // dense: [N/128, K/128]; g1u1: [E, 2I/128, K/128]; down: [E, N/128, K/128]
-  const int32_t* sorted_ids;
-  const int32_t* sorted_eids;
-  const int32_t* num_valid;
-  const float* sorted_w;
-  int M;                   // dense rows
-  int N;                   // output columns: dense N, g1u1 I, down H
-  int K;
-  int T, topk;
-  uint16_t* c;             // dense out
-  int64_t ldc;
-  uint8_t* h8;             // g1u1 out [max_sorted, N]
-  float* h_scale;          // g1u1 out [max_sorted, N/128]
-  float* y;                // down staging [T*topk, N] fp32
-  const float* smooth;     // g1u1: optional per-expert channel factors for h [E, N] (fc2 smoothing)
-  int splits, kbs;         // dense split-K: K blocks [ks*kbs, ks*kbs+kbs) per split ks
-  int out_f16;             // dense: c holds fp16 (1) or bf16 (0) bits
-  float* part;             // dense split-K partial sums [splits, M, N] fp32
-};
 
 // Tile configuration.  BNB = B rows staged per workgroup (g1u1: 128 gate + 128 up).
 template <int MODE, int BM_, int BNB_, int NW_, int WM_, int S_>
@@ -82,92 +56,32 @@ struct Cfg {
   static constexpr int kBQ = BNB / 8;
   static constexpr int kAQ = (kAQ0 + kBQ + NW - 1) / NW * NW - kBQ;  // padded: every wave issues the same count
   static constexpr int kQW = (kAQ + kBQ) / NW;        // 16-byte DMAs per lane per stage
-  static constexpr int kLoadsPerStage = kQW + 1;      // + the wave's A-scale DMA
+  static constexpr int kSD = (kWTM + 63) / 64;        // A-scale DMAs per wave and stage (64 rows each)
+  static constexpr int kLoadsPerStage = kQW + kSD;
   static constexpr int kAOff = 0;
   static constexpr int kBOff = kAQ * 1024;
   static constexpr int kSOff = kBOff + kBQ * 1024;
-  static constexpr int kStage = kSOff + NW * 256;     // 64 fp32 A scales per wave
+  static constexpr int kStage = kSOff + NW * kSD * 256;  // 64 fp32 A scales per scale DMA
   static constexpr int kLds = S * kStage;
-  // g1u1 epilogue: threads per output row (each takes 128 / kQPR columns)
-  static constexpr int kQPR = kThreads / BM >= 8 ? 8 : kThreads / BM;
+  // more than 4 row tiles per wave: A fragments are read one row tile at a time,
+  // just ahead of the 4 MFMAs that use them, instead of all at the start of a step
+  static constexpr bool kStreamA = kWTM / 16 > 4;
+  // g1u1 epilogue: rows per pass (a pass stages its fp32 gate/up rows in LDS) and
+  // threads per output row (each takes 128 / kQPR columns)
+  static constexpr int kEpR = BM < 128 ? BM : 128;
+  static constexpr int kQPR = kThreads / kEpR >= 8 ? 8 : kThreads / kEpR;
   static_assert(MODE != kG1U1 || (kQPR >= 1 && 128 % kQPR == 0 && 128 / kQPR % 16 == 0), "g1u1 epilogue split");
-  static constexpr int kRed = kQPR > kWN ? kQPR : kWN;
+  static_assert(BM % kEpR == 0 && (kWTM <= kEpR ? kEpR % kWTM == 0 : kWTM % kEpR == 0), "epilogue passes");
+  static constexpr int kRed = kQPR;
   static_assert(kWTM % 16 == 0 && kWTNB % 16 == 0, "wave tile must be whole MFMA tiles");
   static_assert(kWTNB <= 128 && 128 % kWTNB == 0, "a wave's columns lie in one 128-column scale block");
-  static_assert(kWTM <= 64, "one A-scale DMA per wave covers 64 rows");
+  static_assert(kWTM <= 128, "at most two A-scale DMAs per wave");
   static_assert(MODE != kG1U1 || BNB == 256, "g1u1 stages 128 gate and 128 up rows");
   static_assert(kWN % kParts == 0, "gate and up waves split evenly");
   static_assert(S >= 2 && S <= 4 && 2 * kLoadsPerStage < 64, "pipeline depth");
+  static_assert(kLds + BM * 4 + kRed * kEpR * 4 <= 160 * 1024, "LDS of one workgroup");
 };
 
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// LDS-DMA: every lane moves 16 (or 4) bytes from base + its 32-bit offset to
-// LDS[m0 + 16*lane] (or 4*lane); base is wave-uniform (SGPRs), so advancing a
-// stream costs scalar adds only.  Issued from asm so that the compiler does
-// not drain the DMA queue before each LDS read; completion is tracked
-// explicitly with vm_wait.  No output registers.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0)
-               : "memory");
-}
-__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(m0)
-               : "memory");
-}
-
-__device__ __forceinline__ const uint8_t* uniform_ptr(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
-}
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
-
-// wait until at most a*PER of this wave's DMAs are in flight, a in [0, 2]
-template <int PER>
-__device__ __forceinline__ void vm_wait_stages(int a) {
-  if (a >= 2) {
-    vm_wait<2 * PER>();
-  } else if (a == 1) {
-    vm_wait<PER>();
-  } else {
-    vm_wait<0>();
-  }
-}
-
-__device__ __forceinline__ void lgkm_wait0() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0), vmcnt and expcnt untouched
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void barrier_only() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ int swz(int r, int ch) { return r * 128 + ((ch ^ (r & 7)) << 4); }
-
-// MFMA operand for the 16 rows starting at r0: lane l holds row r0 + l%16 with
-// K chunks l/16 (low half) and 4 + l/16 (high half; its slot differs in bit 2).
-__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int r0, int lane) {
-  const int off = swz(r0 + (lane & 15), lane >> 4);
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + off);
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + (off ^ 64));
-  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
 
 // PK (dense only): K is not a multiple of 128, so the last K block holds
 // K % 128 bytes of each row.  The DMA pipeline walks the full blocks; the
@@ -189,7 +103,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   constexpr bool kBUni = BSH && C::BM == 128;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLds];
   __shared__ int rowinfo[C::BM];
-  __shared__ float red[C::kRed][C::BM];
+  __shared__ float red[C::kRed][C::kEpR];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in SGPRs
@@ -312,7 +226,9 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     const int r = qq * 8 + (lane >> 3);
     const int ch = (lane & 7) ^ (r & 7);
     if (is_a) {
-      voff[j] = (uint32_t)(a_row(r < C::BM ? r : 0) * g.K + ch * 16);
+      // a block of 8 rows that holds only padding (or rows past M) reads 16 bytes of the
+      // first row into every slot instead: its rows are never used
+      voff[j] = qq * 8 < nrows ? (uint32_t)(a_row(r < C::BM ? r : 0) * g.K + ch * 16) : 0u;
     } else if constexpr (kBUni) {
       voff[j] = 0;  // unused: addressed from the wave-uniform base
     } else if constexpr (BSH) {
@@ -323,16 +239,21 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     }
   }
   const uint32_t lane16 = (uint32_t)lane * 16;
-  const int my_row = wm * C::kWTM + (lane < C::kWTM ? lane : 0);
-  const uint32_t soff = (uint32_t)(a_row(my_row) * g.ssm * 4);
+  // scale DMA d of this wave moves the A scales of its rows [64d, 64d + 64)
+  uint32_t soff[C::kSD];
+#pragma unroll
+  for (int d = 0; d < C::kSD; ++d) {
+    const int rr = d * 64 + lane;
+    soff[d] = (uint32_t)(a_row(wm * C::kWTM + (rr < C::kWTM ? rr : 0)) * g.ssm * 4);
+  }
   const uint8_t* s_base = uniform_ptr(g.a_scale);
-  const int sofs = C::kSOff + w * 256;
+  const int sofs = C::kSOff + w * C::kSD * 256;
 
   vm_wait<0>();  // every ordinary load lands before the first DMA is queued
 
   const uint32_t lds0 = lds_addr(lds);
   // DMA j of this wave for K block kb into LDS stage `stage`: j < kQW moves A/B
-  // rows, j == kQW the wave's A scales
+  // rows, j >= kQW the wave's A scales
   // (every operand but voff / soff is wave-uniform: addresses and m0 stay in SGPRs)
   auto issue_one = [&](int stage, int kb, int j) {
     const uint32_t base = lds0 + stage * C::kStage;
@@ -355,12 +276,13 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
         dma16((q < C::kAQ ? a_base : b_base) + kg * 128, voff[j], base + q * 1024);
       }
     } else {
-      dma4(s_base + kg * g.sskb * 4, soff, base + sofs);
+      const int d = j - C::kQW;
+      dma4(s_base + kg * g.sskb * 4, soff[d], base + sofs + d * 256);
     }
   };
   auto issue = [&](int stage, int kb) {
 #pragma unroll
-    for (int j = 0; j <= C::kQW; ++j) issue_one(stage, kb, j);
+    for (int j = 0; j < C::kLoadsPerStage; ++j) issue_one(stage, kb, j);
   };
 
   v4f acc[C::kTM][C::kTN];
@@ -394,29 +316,41 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
       const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? sbv0 : sbv1), kb & 63));
       v8i av[TMV];
       v4f s4[TMV];
-#pragma unroll
-      for (int tm = 0; tm < TMV; ++tm) {
+      auto load_a = [&](int tm) {
         av[tm] = lds_frag(st + C::kAOff, wm * C::kWTM + tm * 16, lane);
         s4[tm] = *reinterpret_cast<const v4f*>(st + sofs + (tm * 16 + 4 * lg) * 4) * sb;
+      };
+      if constexpr (!C::kStreamA) {
+#pragma unroll
+        for (int tm = 0; tm < TMV; ++tm) load_a(tm);
+      } else {
+        load_a(0);
       }
       v8i bv[C::kTN];
 #pragma unroll
       for (int tn = 0; tn < C::kTN; ++tn) bv[tn] = lds_frag(st + C::kBOff, wn * C::kWTNB + tn * 16, lane);
       // rolling window: tile q is issued, tile q-2 is folded.  The refill DMAs of
       // the stage freed by the barrier are spread between the MFMAs (DMA j after
-      // MFMA j * kGap), so a wave never stalls on a burst of DMA issues.
+      // MFMA j * kGap), so a wave never stalls on a burst of DMA issues.  Tile
+      // order: row tile fastest, or (kStreamA) column tile fastest so that one row
+      // tile's fragment serves 4 consecutive MFMAs and the next is read meanwhile.
       constexpr int NQ = TMV * C::kTN;
-      constexpr int kGap = NQ / (C::kQW + 1) > 0 ? NQ / (C::kQW + 1) : 1;
+      constexpr int kGap = NQ / C::kLoadsPerStage > 0 ? NQ / C::kLoadsPerStage : 1;
+      auto tile_m = [](int q) { return C::kStreamA ? q / C::kTN : q % TMV; };
+      auto tile_n = [](int q) { return C::kStreamA ? q % C::kTN : q / TMV; };
       v4f tq[3];
 #pragma unroll
       for (int q = 0; q < NQ + 2; ++q) {
-        if (q < NQ) tq[q % 3] = mfma16x16x128_fp8(av[q % TMV], bv[q / TMV], v4f{0.f, 0.f, 0.f, 0.f});
+        if constexpr (C::kStreamA) {
+          if (q < NQ && tile_n(q) == 0 && tile_m(q) + 1 < TMV) load_a(tile_m(q) + 1);
+        }
+        if (q < NQ) tq[q % 3] = mfma16x16x128_fp8(av[tile_m(q)], bv[tile_n(q)], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int j = 0; j <= C::kQW; ++j)
+        for (int j = 0; j < C::kLoadsPerStage; ++j)
           if (refill && (j * kGap < NQ + 1 ? j * kGap : NQ + 1) == q) issue_one(nstage, nkb, j);
         if (q >= 2) {
           const int p = q - 2;
-          acc[p % TMV][p / TMV] += tq[p % 3] * s4[p % TMV];
+          acc[tile_m(p)][tile_n(p)] += tq[p % 3] * s4[tile_m(p)];
         }
       }
     }
@@ -450,30 +384,37 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
           if (chb < kt) v = *reinterpret_cast<const u32x4*>((q < C::kAQ ? a_base : b_base) + kg * 128 + voff[j]);
           *reinterpret_cast<u32x4*>(lds + q * 1024 + lane * 16) = v;
         }
-        *reinterpret_cast<float*>(lds + sofs + lane * 4) =
-            *reinterpret_cast<const float*>(s_base + kg * g.sskb * 4 + soff);
+#pragma unroll
+        for (int d = 0; d < C::kSD; ++d)
+          *reinterpret_cast<float*>(lds + sofs + d * 256 + lane * 4) =
+              *reinterpret_cast<const float*>(s_base + kg * g.sskb * 4 + soff[d]);
         lgkm_wait0();
         step(KBp, 0, tmv_c, std::integral_constant<int, 0>{});
       }
     }
   };
-  static_assert(C::kTM <= 4, "row tiles per wave");
-  static_assert(C::BM * (C::BNB + 4) * 4 <= C::kLds, "padded fp32 output tile fits the pipeline LDS");
+  static_assert(C::kTM <= 8, "row tiles per wave");
   switch (tm_live) {
     case 0: kloop(std::integral_constant<int, 0>{}); break;
     case 1: kloop(std::integral_constant<int, 1>{}); break;
     case 2: if constexpr (C::kTM >= 2) kloop(std::integral_constant<int, 2>{}); break;
     case 3: if constexpr (C::kTM >= 3) kloop(std::integral_constant<int, 3>{}); break;
-    default: if constexpr (C::kTM >= 4) kloop(std::integral_constant<int, 4>{}); break;
+    case 4: if constexpr (C::kTM >= 4) kloop(std::integral_constant<int, 4>{}); break;
+    case 5: if constexpr (C::kTM >= 5) kloop(std::integral_constant<int, 5>{}); break;
+    case 6: if constexpr (C::kTM >= 6) kloop(std::integral_constant<int, 6>{}); break;
+    case 7: if constexpr (C::kTM >= 7) kloop(std::integral_constant<int, 7>{}); break;
+    default: if constexpr (C::kTM >= 8) kloop(std::integral_constant<int, 8>{}); break;
   }
   vm_wait<0>();
   __syncthreads();
 
   // ---- epilogues (LDS is free again)
-  if (MODE == kDense && g.splits > 1) {
+  if (MODE == kDense && C::BM <= 128 && g.splits > 1) {
     // split-K partial: fp32 tile [BM][BNB] in LDS (rows padded by 16 bytes so that
     // rows 4 apart do not share banks), then 16-byte stores into part[ks]
+    // (the host splits K only for M tiles of at most 64 rows)
     constexpr int RS = C::BNB + 4;
+    static_assert(C::BM > 128 || C::BM * RS * 4 <= C::kLds, "padded fp32 output tile fits the pipeline LDS");
     float* ob = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int tm = 0; tm < C::kTM; ++tm)
@@ -495,6 +436,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   } else if constexpr (MODE == kDense) {
     // bf16 tile [BM][BNB] in LDS (rows padded by 16 bytes), then 16-byte row stores
     constexpr int RS = C::BNB + 8;
+    static_assert(C::BM * RS * 2 <= C::kLds, "bf16 output tile fits the pipeline LDS");
     uint16_t* ob = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
     for (int tm = 0; tm < C::kTM; ++tm)
@@ -532,59 +474,68 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
       }
   } else {
     // Both parts stage their fp32 tiles in LDS as rows [gate 128 | up 128] (row
-    // stride kFS words: conflict-free stores).  Then each thread takes kCPI
-    // consecutive columns of one row: h = SiLU(gate) * up, the row's amax over its
-    // 128 columns (partial maxima through red), 1x128 requantisation, and 16-byte
-    // stores of the codes straight to h8.
+    // stride kFS words: conflict-free stores), kEpR rows per pass.  Then each thread
+    // takes kCPI consecutive columns of one row: h = SiLU(gate) * up, the row's amax
+    // over its 128 columns (partial maxima through red), 1x128 requantisation, and
+    // 16-byte stores of the codes straight to h8.
     constexpr int kFS = 2 * 128 + 4;
+    constexpr int kEpR = C::kEpR;
     constexpr int kQPR = C::kQPR, kCPI = 128 / kQPR;
-    static_assert(C::BM * kFS * 4 <= C::kLds, "gate/up tile fits the pipeline LDS");
+    static_assert(kEpR * kFS * 4 <= C::kLds, "gate/up rows of a pass fit the pipeline LDS");
     float* F = reinterpret_cast<float*>(lds);
-#pragma unroll
-    for (int tm = 0; tm < C::kTM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < C::kTN; ++tn)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          F[(wm * C::kWTM + tm * 16 + 4 * lg + i) * kFS + part * 128 + colofs + tn * 16 + lr] = acc[tm][tn][i];
-    __syncthreads();
-    const int r = tid % C::BM, qc = tid / C::BM;  // row and column group of this thread
+    const int r = tid % kEpR, qc = tid / kEpR;  // row (within a pass) and column group of this thread
     const bool active = qc < kQPR;
-    float h[kCPI];
-    if (active) {
-      float mx = 0.0f;
-      // fc2 smoothing factors of this expert's columns (uniform branch: pointer or none)
-      const float* sm = g.smooth ? g.smooth + (int64_t)expert * g.N + nt * 128 + qc * kCPI : nullptr;
 #pragma unroll
-      for (int v = 0; v < kCPI; v += 4) {
-        const v4f gt = *reinterpret_cast<const v4f*>(F + r * kFS + qc * kCPI + v);
-        const v4f up = *reinterpret_cast<const v4f*>(F + r * kFS + 128 + qc * kCPI + v);
-        const v4f f = sm ? *reinterpret_cast<const v4f*>(sm + v) : v4f{1.f, 1.f, 1.f, 1.f};
+    for (int pass = 0; pass < C::BM / kEpR; ++pass) {
+      if (pass > 0) __syncthreads();  // the previous pass has read F and red
+      const int wrow0 = wm * C::kWTM - pass * kEpR;  // this wave's first row inside the pass
+      if (wrow0 >= 0 && wrow0 < kEpR) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h[v + i] = gt[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-gt[i])) * up[i];
-          if (sm) h[v + i] = h[v + i] * f[i];
-          mx = fmaxf(mx, fabsf(h[v + i]));
-        }
+        for (int tm = 0; tm < C::kTM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < C::kTN; ++tn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              F[(wrow0 + tm * 16 + 4 * lg + i) * kFS + part * 128 + colofs + tn * 16 + lr] = acc[tm][tn][i];
       }
-      red[qc][r] = mx;
-    }
-    __syncthreads();
-    if (active && rowinfo[r] < npairs) {
-      float amax = red[0][r];
+      __syncthreads();
+      const int rt = pass * kEpR + r;  // row inside the tile
+      float h[kCPI];
+      if (active) {
+        float mx = 0.0f;
+        // fc2 smoothing factors of this expert's columns (uniform branch: pointer or none)
+        const float* sm = g.smooth ? g.smooth + (int64_t)expert * g.N + nt * 128 + qc * kCPI : nullptr;
 #pragma unroll
-      for (int k2 = 1; k2 < kQPR; ++k2) amax = fmaxf(amax, red[k2][r]);
-      const float sc = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
-      uint32_t wds[kCPI / 4];
+        for (int v = 0; v < kCPI; v += 4) {
+          const v4f gt = *reinterpret_cast<const v4f*>(F + r * kFS + qc * kCPI + v);
+          const v4f up = *reinterpret_cast<const v4f*>(F + r * kFS + 128 + qc * kCPI + v);
+          const v4f f = sm ? *reinterpret_cast<const v4f*>(sm + v) : v4f{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-      for (int v = 0; v < kCPI / 4; ++v)
-        wds[v] = f32_to_e4m3(h[4 * v] / sc) | (f32_to_e4m3(h[4 * v + 1] / sc) << 8) |
-                 (f32_to_e4m3(h[4 * v + 2] / sc) << 16) | (f32_to_e4m3(h[4 * v + 3] / sc) << 24);
-      uint8_t* dst = g.h8 + (row0 + r) * g.N + nt * 128 + qc * kCPI;
+          for (int i = 0; i < 4; ++i) {
+            h[v + i] = gt[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-gt[i])) * up[i];
+            if (sm) h[v + i] = h[v + i] * f[i];
+            mx = fmaxf(mx, fabsf(h[v + i]));
+          }
+        }
+        red[qc][r] = mx;
+      }
+      __syncthreads();
+      if (active && rowinfo[rt] < npairs) {
+        float amax = red[0][r];
 #pragma unroll
-      for (int v = 0; v < kCPI / 16; ++v)
-        *reinterpret_cast<u32x4*>(dst + 16 * v) = u32x4{wds[4 * v], wds[4 * v + 1], wds[4 * v + 2], wds[4 * v + 3]};
-      if (qc == 0) g.h_scale[(row0 + r) * (g.N / 128) + nt] = sc;
+        for (int k2 = 1; k2 < kQPR; ++k2) amax = fmaxf(amax, red[k2][r]);
+        const float sc = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+        uint32_t wds[kCPI / 4];
+#pragma unroll
+        for (int v = 0; v < kCPI / 4; ++v)
+          wds[v] = f32_to_e4m3(h[4 * v] / sc) | (f32_to_e4m3(h[4 * v + 1] / sc) << 8) |
+                   (f32_to_e4m3(h[4 * v + 2] / sc) << 16) | (f32_to_e4m3(h[4 * v + 3] / sc) << 24);
+        uint8_t* dst = g.h8 + (row0 + rt) * g.N + nt * 128 + qc * kCPI;
+#pragma unroll
+        for (int v = 0; v < kCPI / 16; ++v)
+          *reinterpret_cast<u32x4*>(dst + 16 * v) = u32x4{wds[4 * v], wds[4 * v + 1], wds[4 * v + 2], wds[4 * v + 3]};
+        if (qc == 0) g.h_scale[(row0 + rt) * (g.N / 128) + nt] = sc;
+      }
     }
   }
 }
@@ -681,6 +632,13 @@ int launch_gemm(const GemmArgs& g, int bm, int64_t mblocks, hipStream_t stream) 
     case 32: return launch_cfg<Cfg<MODE, 32, BNB, 4, 1, 4>, MODE, PK, BSH>(g, mblocks, stream);
     case 64: return launch_cfg<Cfg<MODE, 64, BNB, 4, 1, 3>, MODE, PK, BSH>(g, mblocks, stream);
     case 128: return launch_cfg<Cfg<MODE, 128, BNB, 8, 2, 3>, MODE, PK, BSH>(g, mblocks, stream);
+    case 256:
+      // grouped GEMMs on 256 x 256 tiles (gemm_big.hip)
+      if constexpr (PK || BNB != 256 || MODE == kDense) {
+        return MOE355_EUNSUPPORTED;
+      } else {
+        return launch_big<MODE, BSH>(g, mblocks, stream);
+      }
     default: return MOE355_EUNSUPPORTED;
   }
 }

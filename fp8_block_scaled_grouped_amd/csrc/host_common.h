@@ -16,7 +16,7 @@ inline int launch_status() {
 
 inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+inline bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 }  // namespace moe355
 

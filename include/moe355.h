@@ -79,7 +79,7 @@ int grouped_topk(const void* logits, int logits_bf16, int64_t ld_logits, const f
  *                     rounded up to block_m;
  *   max_blocks      = max_sorted / block_m = capacity of sorted_expert_ids;
  *   workspace_bytes = device scratch moe_sort needs.
- * Any output pointer may be NULL.  block_m must be 16, 32, 64 or 128.
+ * Any output pointer may be NULL.  block_m must be 16, 32, 64, 128 or 256.
  */
 int moe_sort_sizes(int T, int topk, int E, int block_m,
                    int64_t* max_sorted, int64_t* max_blocks, size_t* workspace_bytes);
@@ -155,7 +155,7 @@ int fp8_quant_1x128(const uint16_t* x, int64_t ld_x, int M, int K,
  *           caller folds the inverse factors into w2).
  *           Padding rows and rows at or beyond num_valid are not written (nothing
  *           is written when num_valid is -1).
- * H % 128 == 0, I % 128 == 0, block_m in {16, 32, 64, 128}; a8, w1, h8 16-byte aligned.
+ * H % 128 == 0, I % 128 == 0, block_m in {16, 32, 64, 128, 256}; a8, w1, h8 16-byte aligned.
  * T * sstride_m * 4 < 2^32 (the scale reads take 32-bit byte offsets), else MOE355_EUNSUPPORTED.
  */
 int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale,

@@ -46,7 +46,8 @@ def test_strerror(lib):
 def test_sort_sizes(lib):
     from fp8_block_scaled_grouped_amd import moe355
     import oracle
-    for T, k, E, BM in [(16, 4, 16, 16), (64, 8, 256, 16), (8192, 8, 256, 128), (4096, 8, 256, 64), (0, 8, 256, 32)]:
+    for T, k, E, BM in [(16, 4, 16, 16), (64, 8, 256, 16), (8192, 8, 256, 128), (4096, 8, 256, 64), (0, 8, 256, 32),
+                        (8192, 8, 256, 256)]:
         ms, mb, ws = moe355.moe_sort_sizes(T, k, E, BM)
         assert (ms, mb) == oracle.sort.max_sizes(T, k, E, BM)
         assert ws > 0

@@ -121,7 +121,7 @@ def _check_sort(m, ids, w, E, BM, ld_extra=0):
     assert np.array_equal(seid.cpu().numpy()[:P // BM], rseid)
 
 
-@pytest.mark.parametrize("BM", [16, 32, 64, 128])
+@pytest.mark.parametrize("BM", [16, 32, 64, 128, 256])
 def test_sort_bitexact_tiny_routing(m, tiny, BM):
     cfg, x = tiny
     w, ids = oracle_routing(x, cfg)
@@ -129,7 +129,8 @@ def test_sort_bitexact_tiny_routing(m, tiny, BM):
 
 
 @pytest.mark.parametrize("T,k,E,BM", [(1, 1, 4, 16), (1000, 8, 256, 64), (300, 3, 1024, 16), (4096, 8, 256, 128),
-                                      (2048, 8, 256, 32), (2049, 8, 256, 16), (5000, 4, 1000, 64)])
+                                      (2048, 8, 256, 32), (2049, 8, 256, 16), (5000, 4, 1000, 64),
+                                      (4096, 8, 256, 256), (3000, 8, 64, 256)])
 def test_sort_bitexact_random(m, T, k, E, BM):
     rng = np.random.default_rng(T + E)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
@@ -158,7 +159,7 @@ def _tiny_stage_inputs(tiny, BM):
     return cfg, x, w, ids, (pad(sid, cfg.T * cfg.topk), pad(sw, np.float32(0)), pad(seid, 0), P), a8, sa
 
 
-@pytest.mark.parametrize("BM", [16, 32, 64, 128])
+@pytest.mark.parametrize("BM", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("smooth", [False, True], ids=["plain", "smooth"])
 def test_g1u1_stage_tiny(m, tiny, BM, smooth):
     cfg, x, w, ids, (sid, sw, seid, P), a8, sa = _tiny_stage_inputs(tiny, BM)
@@ -176,7 +177,7 @@ def test_g1u1_stage_tiny(m, tiny, BM, smooth):
     check_requant(np_u8(h8)[rows], hs.cpu().numpy()[rows], h_ref[rows])
 
 
-@pytest.mark.parametrize("BM", [16, 64])
+@pytest.mark.parametrize("BM", [16, 64, 256])
 def test_down_stage_tiny(m, tiny, BM):
     cfg, x, w, ids, (sid, sw, seid, P), a8, sa = _tiny_stage_inputs(tiny, BM)
     h8, hs, _, valid = oracle.moe.g1u1(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), sid, seid, P, cfg.topk, BM)
@@ -223,7 +224,9 @@ def test_layer_tiny_deterministic(m, tiny):
 
 # (5, 1024, 4096): 16 splits of 2 K blocks; (33, 256, 1664): 3 splits of 5, 5, 3 K blocks
 @pytest.mark.parametrize("M,N,K", [(1, 384, 512), (37, 384, 512), (128, 256, 1024), (200, 128, 256), (16, 2048, 7168),
-                                   (5, 1024, 4096), (33, 256, 1664)])
+                                   (5, 1024, 4096), (33, 256, 1664),
+                                   # 256-row tiles (M of 512 and more): ragged M, two K lengths
+                                   (600, 512, 1024), (1030, 768, 2048)])
 @pytest.mark.parametrize("layout", ["row", "kblock"])
 @pytest.mark.parametrize("split", [True, False], ids=["ws", "nows"])
 def test_dense_small(m, M, N, K, layout, split):
@@ -233,12 +236,14 @@ def test_dense_small(m, M, N, K, layout, split):
     sa_dev = torch.from_numpy(sa if layout == "row" else np.ascontiguousarray(sa.T)).to(DEV)
     ws = None
     if split:
-        # garbage in the workspace must not matter
+        # garbage in the workspace must not matter; two calls in a row on the same workspace
         nws = m.gemm_fp8_blockscale_workspace(M, N, K)
         ws = torch.full((max(nws, 16),), 0x7F, dtype=torch.uint8, device=DEV)
-    c = m.gemm_fp8_blockscale(torch.from_numpy(a8).to(DEV), sa_dev, d["b"].to(DEV), d["b_scale"].to(DEV),
-                              scale_layout=layout, workspace=ws if split else False)
+    args = (torch.from_numpy(a8).to(DEV), sa_dev, d["b"].to(DEV), d["b_scale"].to(DEV))
+    c = m.gemm_fp8_blockscale(*args, scale_layout=layout, workspace=ws if split else False).clone()
+    c2 = m.gemm_fp8_blockscale(*args, scale_layout=layout, workspace=ws if split else False)
     torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), c2.view(torch.int16))
     ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
     assert_rel_max(f32_of_bf16(c), ref, what="dense %dx%dx%d" % (M, N, K))
 
@@ -247,7 +252,7 @@ def test_dense_small(m, M, N, K, layout, split):
 # bytes past the last full block), both with 128-row tiles, K below one block, split-K
 # with the partial block in the last split
 @pytest.mark.parametrize("M,N,K", [(5, 576, 1024), (37, 256, 1040), (130, 200, 208), (1, 136, 64),
-                                   (8, 1000, 4112), (64, 4104, 7184), (300, 520, 400)])
+                                   (8, 1000, 4112), (64, 4104, 7184), (300, 520, 400), (700, 512, 1040)])
 @pytest.mark.parametrize("split", [True, False], ids=["ws", "nows"])
 def test_dense_partial_blocks(m, M, N, K, split):
     from fp8_block_scaled_grouped_amd import inputs
@@ -268,7 +273,8 @@ def test_dense_partial_blocks(m, M, N, K, split):
 
 # more than 128 K blocks: always split (a workgroup holds the scales of at most 128),
 # also at M above 64; with partial N / K as well
-@pytest.mark.parametrize("M,N,K", [(37, 256, 18432), (300, 512, 16512), (1, 576, 24576), (130, 136, 16400)])
+@pytest.mark.parametrize("M,N,K", [(37, 256, 18432), (300, 512, 16512), (1, 576, 24576), (130, 136, 16400),
+                                   (600, 512, 16512)])
 def test_dense_long_k(m, M, N, K):
     from fp8_block_scaled_grouped_amd import inputs
     print("dense long K", M, N, K, flush=True)
@@ -325,7 +331,7 @@ def test_dense_preshuffled_bitwise(m, M, N, K):
     assert_rel_max(f32_of_bf16(c1), ref, what="dense preshuffled %dx%dx%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("BM", [16, 32, 64, 128])
+@pytest.mark.parametrize("BM", [16, 32, 64, 128, 256])
 def test_layer_tiny_preshuffled_bitwise(m, tiny, BM):
     cfg, x = tiny
     g = {k: v.to(DEV) for k, v in x.items()}

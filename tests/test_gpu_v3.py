@@ -112,7 +112,8 @@ def host_w(weights):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,block_m", [("decode", 16), ("decode", 32), ("decode", 128), ("prefill", 128),
-                                          ("prefill", 64), ("skew", 128), ("skew", 64)])
+                                          ("prefill", 64), ("prefill", 256), ("skew", 128), ("skew", 64),
+                                          ("skew", 256)])
 def test_layer_all_tokens(m, weights, host_w, name, block_m):
     """The whole layer against the oracle on every token: the bf16 output of all T tokens
     (max|gpu - ref| <= 1e-2 max|ref|) and the requantised h of every routed pair."""
