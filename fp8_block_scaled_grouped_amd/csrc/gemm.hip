@@ -31,6 +31,7 @@
 //          scaled by its routing weight and stored per flat pair; a second
 //          kernel sums each token's pairs in ascending order into bf16.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -871,6 +872,54 @@ extern "C" int gemm_fp8_blockscale_wpreshuffle(const uint8_t* a8, const float* a
                                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return dense_gemm(a8, a_scale, sstride_m, sstride_kb, b8, b_scale, M, N, K, c, ldc, out_fp16, workspace,
                     workspace_bytes, stream, true);
+}
+
+// Static device scratch for gemm_fp8_blockscale_noalloc: the split-K partial sums.
+// Host code never uses this name as an address: the address on each device comes
+// from hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[MOE355_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's copy of `scratch` (looked up on its first use).
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE355_ELAUNCH;
+  MOE355_CHECK(dev >= 0 && dev < kMaxScratchDevices, MOE355_EUNSUPPORTED);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return MOE355_ELAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE355_OK;
+}
+
+}  // namespace
+
+extern "C" int gemm_fp8_blockscale_noalloc(const uint8_t* a8, const float* a_scale, int64_t sstride_m,
+                                           int64_t sstride_kb, const uint8_t* b8, const float* b_scale, int M, int N,
+                                           int K, uint16_t* c, int64_t ldc, int out_fp16, hipStream_t stream) {
+  // the shape checks of the workspace query come first (host only), then the size rule
+  size_t need = 0;
+  const int st = gemm_fp8_blockscale_workspace(M, N, K, &need);
+  if (st != MOE355_OK) return st;
+  MOE355_CHECK(need <= MOE355_STATIC_SCRATCH_BYTES, MOE355_ESCRATCH);
+  void* ws = nullptr;
+  if (need > 0 && (int64_t)M * N > 0) {
+    const int s2 = device_scratch(&ws);
+    if (s2 != MOE355_OK) return s2;
+  }
+  return dense_gemm(a8, a_scale, sstride_m, sstride_kb, b8, b_scale, M, N, K, c, ldc, out_fp16, ws, need, stream,
+                    false);
 }
 
 extern "C" int moe_fp8_blockscale_g1u1(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb,

@@ -8,6 +8,8 @@ extern "C" const char* moe355_strerror(int status) {
     case MOE355_EUNSUPPORTED: return "moe355: unsupported shape or option";
     case MOE355_EMISALIGNED: return "moe355: pointer or row stride not 16-byte aligned";
     case MOE355_ELAUNCH: return "moe355: kernel launch failed";
+    case MOE355_ESCRATCH:
+      return "moe355: the call needs more device scratch than the library's static scratch array holds";
     default: return "moe355: unknown status";
   }
 }

@@ -35,6 +35,7 @@ _SIGNATURES = {
     "gemm_fp8_blockscale": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _vp, _sz, _vp],
                             _i32),
     "shuffle_weight_128x128": ([_vp, _i64, _i32, _vp, _vp], _i32),
+    "gemm_fp8_blockscale_noalloc": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _vp], _i32),
 }
 # the pre-shuffled-weight variants take the same arguments as their plain calls
 for _name in ("gemm_fp8_blockscale", "moe_fp8_blockscale_g1u1", "moe_down_combine"):

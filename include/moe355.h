@@ -40,6 +40,7 @@ extern "C" {
 #define MOE355_EUNSUPPORTED (-2) /* shape or option outside what the kernels implement */
 #define MOE355_EMISALIGNED (-3)  /* a base pointer or row stride breaks the call's alignment rule */
 #define MOE355_ELAUNCH (-4)      /* the HIP runtime reported an error at launch */
+#define MOE355_ESCRATCH (-5)     /* the call needs more than the library's static device scratch */
 
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* moe355_strerror(int status);
@@ -223,6 +224,26 @@ int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale,
                         int M, int N, int K, uint16_t* c, int64_t ldc, int out_fp16,
                         void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
+
+/*
+ * gemm_fp8_blockscale for callers that cannot allocate device memory (code under
+ * HIP-graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, results and errors as gemm_fp8_blockscale with its workspace,
+ * but the split-K partial sums live in a static device array of the library
+ * (MOE355_STATIC_SCRATCH_BYTES per GPU, held by every GPU the library runs on
+ * until the process ends).  The call allocates nothing; a shape whose split-K
+ * partials need more than that array (gemm_fp8_blockscale_workspace) returns
+ * MOE355_ESCRATCH before anything is launched.  All calls on one GPU share its
+ * array: calls that overlap in time on one GPU (other streams, other threads) race.
+ * The first call on a GPU looks up the array's address there (it must be the
+ * current device); a failure of that lookup returns MOE355_ELAUNCH.
+ */
+#define MOE355_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int gemm_fp8_blockscale_noalloc(const uint8_t* a8, const float* a_scale,
+                                int64_t sstride_m, int64_t sstride_kb,
+                                const uint8_t* b8, const float* b_scale,
+                                int M, int N, int K, uint16_t* c, int64_t ldc, int out_fp16,
+                                hipStream_t stream);
 
 /*
  * Pre-shuffled weights ("General Linear Layer": the linear path runs on weights

@@ -39,7 +39,7 @@ def test_every_declared_symbol_exported(lib):
 
 
 def test_strerror(lib):
-    for code in (0, -1, -2, -3, -4, -99):
+    for code in (0, -1, -2, -3, -4, -5, -99):
         assert lib.moe355_strerror(code).decode().startswith("moe355:")
 
 
@@ -109,6 +109,12 @@ def test_invalid_arguments_return_codes(lib):
                                      304, _p(), _p(), None, None) == -2
     assert L.moe_fp8_blockscale_g1u1(_p(), _p(), 1 << 26, 1, _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16,
                                      304, _p(8), _p(), None, None) == -2
+    # the allocation-free dense GEMM: split-K partials beyond its static array -> ESCRATCH
+    # (4096 x 7168 x 18432 always splits K: 235 MB of partials); shape rules as the plain call
+    assert L.gemm_fp8_blockscale_noalloc(_p(), _p(), 144, 1, _p(), _p(), 4096, 7168, 18432, _p(), 7168, 0,
+                                         None) == -5
+    assert L.gemm_fp8_blockscale_noalloc(_p(), _p(), 2, 1, _p(), _p(), 4, 100, 256, _p(), 104, 0, None) == -2
+    assert L.gemm_fp8_blockscale_noalloc(None, None, 2, 1, None, None, 0, 256, 256, None, 256, 0, None) == 0
     # down: workspace too small
     assert L.moe_down_combine(_p(), _p(), _p(), _p(), _p(), _p(), _p(), _p(), 16, 256, 128, 16, 4, 16, 304, _p(),
                               256, _p(), 8, None) == -1
