@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--sweep", choices=["block_m", "dense"], default=None)
     ap.add_argument("--graph", action="store_true",
                     help="also time the layer captured once as a HIP graph and replayed (graph_ms_per_step)")
+    ap.add_argument("--fused", action="store_true",
+                    help="the expert computation as one launch (moe_fp8_blockscale_fused) instead of two calls")
     ap.add_argument("--preshuffle", action="store_true",
                     help="weights permuted once into the 128x128-tile layout (the *_wpreshuffle calls)")
     ap.add_argument("--dense-m", type=int, default=64)
@@ -199,15 +201,16 @@ def moe_inputs(cfg, seed, weights=None):
     return x
 
 
-def time_layer(cfg, x, bm, steps, warmup, preshuffle=False, graph=False, per_call=True):
-    """Time K whole layer steps on the current stream; the g1u1 launch of every step is
-    bracketed by events on the same stream.  Returns a dict of timings and the layer."""
+def time_layer(cfg, x, bm, steps, warmup, preshuffle=False, graph=False, per_call=True, fused=False):
+    """Time K whole layer steps on the current stream; the g1u1 launch of every step (the
+    fused launch with fused=True) is bracketed by events on the same stream.  Returns a
+    dict of timings and the layer."""
     import torch
 
     import fp8_block_scaled_grouped_amd as m
 
     layer = m.MoELayer(cfg, x["bias"], x["w1"], x["w1_scale"], x["w2"], x["w2_scale"], block_m=bm,
-                       preshuffle=preshuffle)
+                       preshuffle=preshuffle, fused=fused)
     hidden, logits = x["hidden"], x["logits"]
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -227,11 +230,16 @@ def time_layer(cfg, x, bm, steps, warmup, preshuffle=False, graph=False, per_cal
         sid, sw, seid, nv = m.moe_sort(layer.topk_ids, layer.topk_w, c.E, bm, layer.sort_out, layer.sort_ws)
         m.fp8_quant_1x128(hidden, layer.a8, layer.a_scale)
         ev[i][0].record(stream)
-        m.moe_fp8_blockscale_g1u1(layer.a8, layer.a_scale, layer.w1, layer.w1_scale, sid, seid, nv, c.topk, bm,
-                                  layer.h8, layer.h_scale, preshuffled=layer.preshuffle)
-        ev[i][1].record(stream)
-        m.moe_down_combine(layer.h8, layer.h_scale, layer.w2, layer.w2_scale, sid, sw, seid, nv, layer.T, c.topk,
-                           bm, layer.out, layer.down_ws, preshuffled=layer.preshuffle)
+        if fused:
+            m.moe_fp8_blockscale_fused(layer.a8, layer.a_scale, layer.w1, layer.w1_scale, layer.w2, layer.w2_scale,
+                                       sid, sw, seid, nv, c.topk, bm, layer.out, layer.fused_ws)
+            ev[i][1].record(stream)
+        else:
+            m.moe_fp8_blockscale_g1u1(layer.a8, layer.a_scale, layer.w1, layer.w1_scale, sid, seid, nv, c.topk, bm,
+                                      layer.h8, layer.h_scale, preshuffled=layer.preshuffle)
+            ev[i][1].record(stream)
+            m.moe_down_combine(layer.h8, layer.h_scale, layer.w2, layer.w2_scale, sid, sw, seid, nv, layer.T,
+                               c.topk, bm, layer.out, layer.down_ws, preshuffled=layer.preshuffle)
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
@@ -258,7 +266,7 @@ def time_layer(cfg, x, bm, steps, warmup, preshuffle=False, graph=False, per_cal
         r["graph_ms"] = g0.elapsed_time(g1) / steps
         del g
 
-    if per_call:
+    if per_call and not fused:
         # per-call breakdown (outside the timed region): events around each of the five calls
         calls = [
             ("grouped_topk", lambda: m.grouped_topk(logits, layer.bias, c.n_group, c.topk_group, c.topk, c.renorm,
@@ -290,9 +298,10 @@ def time_layer(cfg, x, bm, steps, warmup, preshuffle=False, graph=False, per_cal
     return r
 
 
-def moe_report(cfg, bm, tm, workload, seed, preshuffle):
+def moe_report(cfg, bm, tm, workload, seed, preshuffle, fused=False):
     """Bench-line fields of one timed MoE workload: tokens/s, layer TFLOP/s and GB/s, the
-    routing statistics and the roofline of the dominant kernel (moe_fp8_blockscale_g1u1)."""
+    routing statistics and the roofline of the dominant kernel (moe_fp8_blockscale_g1u1, or
+    the fused launch that holds both expert GEMMs)."""
     import torch
     from fp8_block_scaled_grouped_amd import inputs
 
@@ -311,6 +320,12 @@ def moe_report(cfg, bm, tm, workload, seed, preshuffle):
     g1u1_bytes = (n_active * per_expert_w1 + T * H + 4 * T * (H // 128) + 4 * layer.max_sorted
                   + T * k * (I + 4 * (I // 128)))
     g1u1_flops = 2.0 * T * k * 2 * I * H
+    if fused:
+        # the fused launch: both expert GEMMs (w1 and w2 of the routed experts), a8 in, output out
+        per_expert_w2 = H * I + 4 * (H // 128) * (I // 128)
+        g1u1_bytes = n_active * (per_expert_w1 + per_expert_w2) + T * H + 4 * T * (H // 128) + 8 * layer.max_sorted \
+            + 2 * T * H
+        g1u1_flops = inputs.moe_flops(cfg)
     if cfg.T <= 512:
         roof = {"bound": "hbm", "achieved": g1u1_bytes / (g1u1_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
@@ -318,17 +333,17 @@ def moe_report(cfg, bm, tm, workload, seed, preshuffle):
         roof = {"bound": "mfma", "achieved": g1u1_flops / (g1u1_ms * 1e-3) / 1e12, "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "moe_fp8_blockscale_g1u1"
+    roof["kernel"] = "moe_fp8_blockscale_fused" if fused else "moe_fp8_blockscale_g1u1"
     roof["kernel_ms"] = g1u1_ms
     roof["algorithmic_per_launch"] = g1u1_bytes if roof["bound"] == "hbm" else g1u1_flops
-    roof["traffic"] = measured_traffic(workload, "g1u1")
+    roof["traffic"] = None if fused else measured_traffic(workload, "g1u1")
     res = {
         "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
         "config": {"workload": "%s MoE layer: %d tokens, hidden %d, intermediate %d, %d experts / %d groups, "
                                "topk_group %d, top-%d, block_m %d" % (workload, T, H, I, cfg.E, cfg.n_group,
                                                                       cfg.topk_group, k, bm),
                    "tokens": T, "hidden": H, "intermediate": I, "experts": cfg.E, "topk": k, "block_m": bm,
-                   "preshuffled_weights": bool(preshuffle), "seed": seed},
+                   "preshuffled_weights": bool(preshuffle), "fused_expert_launch": bool(fused), "seed": seed},
         "layer_tflops": flops / (ms * 1e-3) / 1e12, "layer_gbs": nbytes / (ms * 1e-3) / 1e9,
         "layer_frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
@@ -348,8 +363,8 @@ def bench_moe(a):
     t0 = time.time()
     x = moe_inputs(cfg, a.seed)
     gen_s = time.time() - t0
-    tm = time_layer(cfg, x, bm, a.steps, a.warmup, a.preshuffle, a.graph)
-    rep = moe_report(cfg, bm, tm, a.workload, a.seed, a.preshuffle)
+    tm = time_layer(cfg, x, bm, a.steps, a.warmup, a.preshuffle, a.graph, fused=a.fused)
+    rep = moe_report(cfg, bm, tm, a.workload, a.seed, a.preshuffle, a.fused)
     res = {"metric": "FP8 blockscale MoE layer tokens/s", "value": rep.pop("tokens_per_s"), "unit": "tokens/s",
            "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": rep.pop("ms_per_step"),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 (fp32 accumulate)",
@@ -362,8 +377,9 @@ def bench_moe(a):
         dcfg = moe_config("decode")
         w = {k: x[k] for k in ("w1", "w1_scale", "w2", "w2_scale")}
         dx = moe_inputs(dcfg, a.seed, weights=w)
-        dtm = time_layer(dcfg, dx, dcfg.block_m, max(a.steps, 20), a.warmup, a.preshuffle, per_call=True)
-        res["decode"] = moe_report(dcfg, dcfg.block_m, dtm, "decode", a.seed, a.preshuffle)
+        dtm = time_layer(dcfg, dx, dcfg.block_m, max(a.steps, 20), a.warmup, a.preshuffle, per_call=True,
+                         fused=a.fused)
+        res["decode"] = moe_report(dcfg, dcfg.block_m, dtm, "decode", a.seed, a.preshuffle, a.fused)
         del dtm
     if not a.no_cpu_baseline:
         # the oracle reads the weights as loaded (row-major), not shuffled copies

@@ -16,6 +16,8 @@ from .moe355 import (  # noqa: F401
     moe_block_m,
     moe_down_combine,
     moe_down_combine_workspace,
+    moe_fp8_blockscale_fused,
+    moe_fp8_blockscale_fused_workspace,
     moe_fp8_blockscale_g1u1,
     moe_sort,
     moe_sort_sizes,

@@ -34,6 +34,8 @@
 #include <mutex>
 #include <type_traits>
 
+#include <hip/hip_cooperative_groups.h>
+
 #include "device_common.h"
 #include "gemm_engine.h"
 #include "host_common.h"
@@ -93,8 +95,19 @@ struct Cfg {
 // BSH: B is stored pre-shuffled (shuffle_weight_128x128): 128-row x 128-byte tiles,
 // the K blocks of a row tile one after another, each row's 16-byte chunks already in
 // their LDS slots, so every B DMA moves one contiguous 1 KB block.
-template <class C, int MODE, bool PK = false, bool BSH = false>
-__global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
+// LDS of one tile of the engine
+template <class C>
+struct GemmSmem {
+  __attribute__((aligned(16))) uint8_t lds[C::kLds];
+  int rowinfo[C::BM];
+  float red[C::kRed][C::kEpR];
+};
+
+// One output tile (tile index `tile_id` of the launch grid) with the workgroup's LDS.
+// Every thread of the workgroup calls it with the same tile; it returns (uniformly)
+// for tiles past the problem.
+template <class C, int MODE, bool PK, bool BSH>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_id, GemmSmem<C>& sm) {
   static_assert(!PK || MODE == kDense, "partial K blocks: dense mode only");
   static_assert(!(PK && BSH), "pre-shuffled B has whole 128x128 tiles");
   constexpr int64_t kBStep = BSH ? 128 * 128 : 128;  // bytes between K blocks of a B row
@@ -102,9 +115,9 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   // in the wave-uniform address for the 128-row tiles (short of VGPRs) and in the
   // per-lane offset for the smaller ones (short of SGPRs)
   constexpr bool kBUni = BSH && C::BM == 128;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLds];
-  __shared__ int rowinfo[C::BM];
-  __shared__ float red[C::kRed][C::kEpR];
+  uint8_t* const lds = sm.lds;
+  int* const rowinfo = sm.rowinfo;
+  float (&red)[C::kRed][C::kEpR] = sm.red;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in SGPRs
@@ -129,7 +142,7 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
     nvalid = g.num_valid[0];
     total = nvalid > 0 ? (int64_t)(nvalid / C::BM) * NT : 0;
   }
-  int64_t tile = blockIdx.x;
+  int64_t tile = tile_id;
   int ks = 0;
   if constexpr (MODE == kDense) {
     ks = (int)(tile / total);
@@ -541,6 +554,12 @@ __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   }
 }
 
+template <class C, int MODE, bool PK = false, bool BSH = false>
+__global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
+  __shared__ GemmSmem<C> sm;
+  gemm_tile<C, MODE, PK, BSH>(g, blockIdx.x, sm);
+}
+
 // out[t, n] = bf16(sum_j y[t*k + j, n]), j ascending, fp32.  Writes nothing when
 // the sort flagged an invalid expert id (num_valid < 0: the pairs were not placed).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int T, int k, int H,
@@ -614,6 +633,68 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// The expert computation of the layer in one cooperative launch ("Blockscale FP8 MoE
+// Computation": the pages run sorted buffers -> moe_buf as a single call): persistent
+// workgroups walk the gate/up tiles, the runtime's grid barrier publishes every h8
+// row (it is a device-scope release/acquire, so rows written on one XCD are read
+// correctly on another), the workgroups walk the down tiles, a second barrier
+// publishes the per-pair staging, and they sum each token's pairs as combine_kernel
+// does.  Each tile runs exactly the arithmetic of the two-launch path.
+struct FusedArgs {
+  GemmArgs gu, dn;             // the gate/up and down launches' arguments
+  int nt_gu, nt_dn;            // their N tiles per sorted block
+  uint16_t* out;
+  int64_t ld_out;
+};
+
+template <class CG, class CD>
+__global__ __launch_bounds__(CG::kThreads) void fused_moe_kernel(FusedArgs f) {
+  static_assert(CG::kThreads == CD::kThreads, "both GEMMs run with the same workgroup size");
+  union Smem {
+    GemmSmem<CG> g;
+    GemmSmem<CD> d;
+  };
+  __shared__ Smem sm;
+  cooperative_groups::grid_group grid = cooperative_groups::this_grid();
+  // only the blocks below num_valid hold rows
+  const int nvalid = f.gu.num_valid[0];
+  const int64_t nblk = nvalid > 0 ? nvalid / CG::BM : 0;
+  for (int64_t t = blockIdx.x; t < nblk * f.nt_gu; t += gridDim.x) {
+    __syncthreads();  // the previous tile is done with the LDS
+    gemm_tile<CG, kG1U1, false, false>(f.gu, t, sm.g);
+  }
+  grid.sync();
+  for (int64_t t = blockIdx.x; t < nblk * f.nt_dn; t += gridDim.x) {
+    __syncthreads();
+    gemm_tile<CD, kDown, false, false>(f.dn, t, sm.d);
+  }
+  grid.sync();
+  if (nvalid < 0) return;  // ids outside [0, E): nothing was placed
+  const int T = f.dn.T, k = f.dn.topk, H = f.dn.N, H8 = H / 8;
+  const int64_t n8 = (int64_t)T * H8;
+  for (int64_t idx = (int64_t)blockIdx.x * CG::kThreads + threadIdx.x; idx < n8;
+       idx += (int64_t)gridDim.x * CG::kThreads) {
+    const int64_t t = idx / H8;
+    const int c8 = (int)(idx - t * H8);
+    float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const float4* p = reinterpret_cast<const float4*>(f.dn.y + ((t * k + j) * (int64_t)H + c8 * 8));
+      const float4 a = p[0], b = p[1];
+      s8[0] += a.x;
+      s8[1] += a.y;
+      s8[2] += a.z;
+      s8[3] += a.w;
+      s8[4] += b.x;
+      s8[5] += b.y;
+      s8[6] += b.z;
+      s8[7] += b.w;
+    }
+    const u32x4 o{f32_to_bf16(s8[0]) | (f32_to_bf16(s8[1]) << 16), f32_to_bf16(s8[2]) | (f32_to_bf16(s8[3]) << 16),
+                  f32_to_bf16(s8[4]) | (f32_to_bf16(s8[5]) << 16), f32_to_bf16(s8[6]) | (f32_to_bf16(s8[7]) << 16)};
+    *reinterpret_cast<u32x4*>(f.out + t * f.ld_out + c8 * 8) = o;
+  }
+}
+
 template <class C, int MODE, bool PK, bool BSH>
 int launch_cfg(const GemmArgs& g, int64_t mblocks, hipStream_t stream) {
   if (MODE != kDense && g.N % C::kOutN != 0) return MOE355_EUNSUPPORTED;
@@ -622,6 +703,41 @@ int launch_cfg(const GemmArgs& g, int64_t mblocks, hipStream_t stream) {
   MOE355_CHECK(grid < (1ll << 31), MOE355_EUNSUPPORTED);
   hipLaunchKernelGGL((bs_gemm_kernel<C, MODE, PK, BSH>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, g);
   return launch_status();
+}
+
+// One cooperative launch of the fused kernel with as many workgroups as the GPU holds
+// at once (the grid barrier needs every workgroup resident).
+template <class CG, class CD>
+int launch_fused_cfg(FusedArgs& f, hipStream_t stream) {
+  const void* kern = reinterpret_cast<const void*>(&fused_moe_kernel<CG, CD>);
+  int dev = -1, ncu = 0, coop = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, CG::kThreads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE355_ELAUNCH;
+  }
+  MOE355_CHECK(coop != 0, MOE355_EUNSUPPORTED);
+  if (per_cu <= 0 || ncu <= 0) return MOE355_ELAUNCH;
+  void* args[] = {&f};
+  if (hipLaunchCooperativeKernel(kern, dim3((unsigned)(per_cu * ncu)), dim3(CG::kThreads), args, 0, stream) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return MOE355_ELAUNCH;
+  }
+  return MOE355_OK;
+}
+
+// the fused kernel runs the tile configurations launch_gemm picks for block_m
+int launch_fused(FusedArgs& f, int bm, hipStream_t stream) {
+  switch (bm) {
+    case 16: return launch_fused_cfg<Cfg<kG1U1, 16, 256, 4, 1, 4>, Cfg<kDown, 16, 256, 4, 1, 4>>(f, stream);
+    case 32: return launch_fused_cfg<Cfg<kG1U1, 32, 256, 4, 1, 4>, Cfg<kDown, 32, 256, 4, 1, 4>>(f, stream);
+    case 64: return launch_fused_cfg<Cfg<kG1U1, 64, 256, 4, 1, 3>, Cfg<kDown, 64, 256, 4, 1, 3>>(f, stream);
+    case 128: return launch_fused_cfg<Cfg<kG1U1, 128, 256, 8, 2, 3>, Cfg<kDown, 128, 256, 8, 2, 3>>(f, stream);
+    default: return MOE355_EUNSUPPORTED;
+  }
 }
 
 // Tile choice per M tile: small tiles stream weights (decode, small M), 128-row
@@ -710,6 +826,38 @@ extern "C" int moe_down_combine_workspace(int T, int H, int topk, size_t* bytes)
 
 namespace {
 
+// fused workspace: h8 [max_sorted, I] | h_scale [max_sorted, I/128] | per-pair staging [T*topk, H]
+struct FusedWs {
+  size_t h8, hs, y, total;
+};
+
+int fused_ws_layout(int T, int H, int I, int E, int topk, int block_m, FusedWs* L) {
+  MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0, MOE355_EINVAL);
+  MOE355_CHECK(I % 128 == 0, MOE355_EUNSUPPORTED);
+  int64_t ms = 0;
+  const int st = moe_sort_sizes(T, topk, E, block_m, &ms, nullptr, nullptr);
+  if (st != MOE355_OK) return st;
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  L->h8 = 0;
+  L->hs = up((size_t)ms * I);
+  L->y = L->hs + up((size_t)ms * (I / 128) * sizeof(float));
+  L->total = L->y + (size_t)T * topk * H * sizeof(float) + 256;
+  return MOE355_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_fp8_blockscale_fused_workspace(int T, int H, int I, int E, int topk, int block_m, size_t* bytes) {
+  MOE355_CHECK(bytes, MOE355_EINVAL);
+  FusedWs L{};
+  const int st = fused_ws_layout(T, H, I, E, topk, block_m, &L);
+  if (st != MOE355_OK) return st;
+  *bytes = L.total;
+  return MOE355_OK;
+}
+
+namespace {
+
 int dense_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb, const uint8_t* b8,
                const float* b_scale, int M, int N, int K, uint16_t* c, int64_t ldc, int out_fp16, void* workspace,
                size_t workspace_bytes, hipStream_t stream, bool bsh) {
@@ -770,24 +918,10 @@ int dense_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64
   return launch_status();
 }
 
-int g1u1_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb, const uint8_t* w1,
-              const float* w1_scale, const int32_t* sorted_ids, const int32_t* sorted_expert_ids,
-              const int32_t* num_valid, int T, int H, int I, int E, int topk, int block_m, int64_t max_sorted,
-              uint8_t* h8, float* h_scale, const float* fc2_smooth_scale, hipStream_t stream, bool bsh) {
-  MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0, MOE355_EINVAL);
-  MOE355_CHECK(H % 128 == 0 && I % 128 == 0 && H <= 16384 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
-  MOE355_CHECK((int64_t)T * H < (1ll << 32) && (int64_t)2 * I * H < (1ll << 32), MOE355_EUNSUPPORTED);
-  const int cap = check_sorted_capacity(T, topk, E, block_m, max_sorted);
-  if (cap != MOE355_OK) return cap;
-  if (T == 0) return MOE355_OK;
-  MOE355_CHECK(a8 && a_scale && w1 && w1_scale && sorted_ids && sorted_expert_ids && num_valid && h8 && h_scale,
-               MOE355_EINVAL);
-  MOE355_CHECK(sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
-  // the A-scale DMA takes a 32-bit byte offset per token row: t * sstride_m * 4
-  MOE355_CHECK((int64_t)T * sstride_m * 4 < (1ll << 32), MOE355_EUNSUPPORTED);
-  MOE355_CHECK(aligned16(a8) && aligned16(w1) && aligned16(h8), MOE355_EMISALIGNED);
-  MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0 && aligned16(fc2_smooth_scale),
-               MOE355_EMISALIGNED);
+GemmArgs g1u1_args(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb, const uint8_t* w1,
+                   const float* w1_scale, const int32_t* sorted_ids, const int32_t* sorted_expert_ids,
+                   const int32_t* num_valid, int T, int H, int I, int topk, uint8_t* h8, float* h_scale,
+                   const float* fc2_smooth_scale) {
   GemmArgs g{};
   g.a = a8;
   g.a_scale = a_scale;
@@ -807,6 +941,53 @@ int g1u1_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_
   g.h_scale = h_scale;
   g.splits = 1;
   g.kbs = H / 128;
+  return g;
+}
+
+GemmArgs down_args(const uint8_t* h8, const float* h_scale, const uint8_t* w2, const float* w2_scale,
+                   const int32_t* sorted_ids, const float* sorted_weights, const int32_t* sorted_expert_ids,
+                   const int32_t* num_valid, int T, int H, int I, int topk, float* y) {
+  GemmArgs g{};
+  g.a = h8;
+  g.a_scale = h_scale;
+  g.ssm = I / 128;
+  g.sskb = 1;
+  g.b = w2;
+  g.b_scale = w2_scale;
+  g.sorted_ids = sorted_ids;
+  g.sorted_eids = sorted_expert_ids;
+  g.num_valid = num_valid;
+  g.sorted_w = sorted_weights;
+  g.N = H;
+  g.K = I;
+  g.T = T;
+  g.topk = topk;
+  g.y = y;
+  g.splits = 1;
+  g.kbs = I / 128;
+  return g;
+}
+
+int g1u1_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb, const uint8_t* w1,
+              const float* w1_scale, const int32_t* sorted_ids, const int32_t* sorted_expert_ids,
+              const int32_t* num_valid, int T, int H, int I, int E, int topk, int block_m, int64_t max_sorted,
+              uint8_t* h8, float* h_scale, const float* fc2_smooth_scale, hipStream_t stream, bool bsh) {
+  MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0, MOE355_EINVAL);
+  MOE355_CHECK(H % 128 == 0 && I % 128 == 0 && H <= 16384 && valid_block_m(block_m), MOE355_EUNSUPPORTED);
+  MOE355_CHECK((int64_t)T * H < (1ll << 32) && (int64_t)2 * I * H < (1ll << 32), MOE355_EUNSUPPORTED);
+  const int cap = check_sorted_capacity(T, topk, E, block_m, max_sorted);
+  if (cap != MOE355_OK) return cap;
+  if (T == 0) return MOE355_OK;
+  MOE355_CHECK(a8 && a_scale && w1 && w1_scale && sorted_ids && sorted_expert_ids && num_valid && h8 && h_scale,
+               MOE355_EINVAL);
+  MOE355_CHECK(sstride_m >= 0 && sstride_kb >= 0, MOE355_EINVAL);
+  // the A-scale DMA takes a 32-bit byte offset per token row: t * sstride_m * 4
+  MOE355_CHECK((int64_t)T * sstride_m * 4 < (1ll << 32), MOE355_EUNSUPPORTED);
+  MOE355_CHECK(aligned16(a8) && aligned16(w1) && aligned16(h8), MOE355_EMISALIGNED);
+  MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0 && aligned16(fc2_smooth_scale),
+               MOE355_EMISALIGNED);
+  const GemmArgs g = g1u1_args(a8, a_scale, sstride_m, sstride_kb, w1, w1_scale, sorted_ids, sorted_expert_ids,
+                               num_valid, T, H, I, topk, h8, h_scale, fc2_smooth_scale);
   return bsh ? launch_gemm<kG1U1, 256, false, true>(g, block_m, max_sorted / block_m, stream)
              : launch_gemm<kG1U1>(g, block_m, max_sorted / block_m, stream);
 }
@@ -829,24 +1010,8 @@ int down_gemm(const uint8_t* h8, const float* h_scale, const uint8_t* w2, const 
   MOE355_CHECK(workspace_bytes >= need, MOE355_EINVAL);
   MOE355_CHECK(aligned16(h8) && aligned16(w2) && aligned16(out) && aligned16(workspace) && ld_out % 8 == 0,
                MOE355_EMISALIGNED);
-  GemmArgs g{};
-  g.a = h8;
-  g.a_scale = h_scale;
-  g.ssm = I / 128;
-  g.sskb = 1;
-  g.b = w2;
-  g.b_scale = w2_scale;
-  g.sorted_ids = sorted_ids;
-  g.sorted_eids = sorted_expert_ids;
-  g.num_valid = num_valid;
-  g.sorted_w = sorted_weights;
-  g.N = H;
-  g.K = I;
-  g.T = T;
-  g.topk = topk;
-  g.y = static_cast<float*>(workspace);
-  g.splits = 1;
-  g.kbs = I / 128;
+  const GemmArgs g = down_args(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sorted_expert_ids, num_valid, T,
+                               H, I, topk, static_cast<float*>(workspace));
   int st = bsh ? launch_gemm<kDown, 256, false, true>(g, block_m, max_sorted / block_m, stream)
                : launch_gemm<kDown>(g, block_m, max_sorted / block_m, stream);
   if (st != MOE355_OK) return st;
@@ -958,4 +1123,47 @@ extern "C" int moe_down_combine_wpreshuffle(const uint8_t* h8, const float* h_sc
                                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return down_gemm(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sorted_expert_ids, num_valid, T, H, I, E,
                    topk, block_m, max_sorted, out, ld_out, workspace, workspace_bytes, stream, true);
+}
+
+extern "C" int moe_fp8_blockscale_fused(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb,
+                                        const uint8_t* w1, const float* w1_scale, const uint8_t* w2,
+                                        const float* w2_scale, const int32_t* sorted_ids, const float* sorted_weights,
+                                        const int32_t* sorted_expert_ids, const int32_t* num_valid, int T, int H,
+                                        int I, int E, int topk, int block_m, int64_t max_sorted,
+                                        const float* fc2_smooth_scale, uint16_t* out, int64_t ld_out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  // the checks of the gate/up and down calls together
+  MOE355_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0 && ld_out >= H, MOE355_EINVAL);
+  MOE355_CHECK(H % 256 == 0 && I % 128 == 0 && H <= 16384 && I <= 16384 && block_m != 256 && valid_block_m(block_m),
+               MOE355_EUNSUPPORTED);
+  MOE355_CHECK((int64_t)T * H < (1ll << 32) && (int64_t)2 * I * H < (1ll << 32) && max_sorted * I < (1ll << 32),
+               MOE355_EUNSUPPORTED);
+  const int cap = check_sorted_capacity(T, topk, E, block_m, max_sorted);
+  if (cap != MOE355_OK) return cap;
+  if (T == 0) return MOE355_OK;
+  MOE355_CHECK(a8 && a_scale && w1 && w1_scale && w2 && w2_scale && sorted_ids && sorted_weights &&
+                   sorted_expert_ids && num_valid && out && workspace && sstride_m >= 0 && sstride_kb >= 0,
+               MOE355_EINVAL);
+  MOE355_CHECK((int64_t)T * sstride_m * 4 < (1ll << 32), MOE355_EUNSUPPORTED);
+  FusedWs L{};
+  const int st = fused_ws_layout(T, H, I, E, topk, block_m, &L);
+  if (st != MOE355_OK) return st;
+  MOE355_CHECK(workspace_bytes >= L.total, MOE355_EINVAL);
+  MOE355_CHECK(aligned16(a8) && aligned16(w1) && aligned16(w2) && aligned16(out) && aligned16(workspace) &&
+                   ld_out % 8 == 0 && (reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0 &&
+                   aligned16(fc2_smooth_scale),
+               MOE355_EMISALIGNED);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* h8 = ws + L.h8;
+  float* hs = reinterpret_cast<float*>(ws + L.hs);
+  FusedArgs f{};
+  f.gu = g1u1_args(a8, a_scale, sstride_m, sstride_kb, w1, w1_scale, sorted_ids, sorted_expert_ids, num_valid, T, H, I,
+                   topk, h8, hs, fc2_smooth_scale);
+  f.dn = down_args(h8, hs, w2, w2_scale, sorted_ids, sorted_weights, sorted_expert_ids, num_valid, T, H, I, topk,
+                   reinterpret_cast<float*>(ws + L.y));
+  f.nt_gu = I / 128;
+  f.nt_dn = H / 256;
+  f.out = out;
+  f.ld_out = ld_out;
+  return launch_fused(f, block_m, stream);
 }

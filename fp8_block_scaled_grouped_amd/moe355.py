@@ -36,6 +36,9 @@ _SIGNATURES = {
                             _i32),
     "shuffle_weight_128x128": ([_vp, _i64, _i32, _vp, _vp], _i32),
     "gemm_fp8_blockscale_noalloc": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _vp], _i32),
+    "moe_fp8_blockscale_fused_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, _PSZ], _i32),
+    "moe_fp8_blockscale_fused": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                  _i32, _i32, _i64, _vp, _vp, _i64, _vp, _sz, _vp], _i32),
 }
 # the pre-shuffled-weight variants take the same arguments as their plain calls
 for _name in ("gemm_fp8_blockscale", "moe_fp8_blockscale_g1u1", "moe_down_combine"):
@@ -292,6 +295,51 @@ def moe_down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sort
     return out
 
 
+def moe_fp8_blockscale_fused_workspace(T, H, I, E, topk, block_m):
+    b = ctypes.c_size_t()
+    _check(lib().moe_fp8_blockscale_fused_workspace(T, H, I, E, topk, block_m, ctypes.byref(b)))
+    return b.value
+
+
+def moe_fp8_blockscale_fused(a8, a_scale, w1, w1_scale, w2, w2_scale, sorted_ids, sorted_weights, sorted_expert_ids,
+                             num_valid, topk, block_m, out=None, workspace=None, scale_layout="row",
+                             fc2_smooth_scale=None):
+    """Gate/up + SiLU*up + requant, down projection and combine in one launch.  Returns bf16 [T, H]."""
+    T, H = a8.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    _need(a8, (T, H), torch.uint8, "a8")
+    _need(w1, (E, 2 * I, H), torch.uint8, "w1")
+    _need(w1_scale, (E, _nblk(2 * I), _nblk(H)), torch.float32, "w1_scale")
+    _need(w2, (E, H, I), torch.uint8, "w2")
+    _need(w2_scale, (E, _nblk(H), _nblk(I)), torch.float32, "w2_scale")
+    ms = sorted_ids.numel()
+    _need(sorted_ids, (ms,), torch.int32, "sorted_ids")
+    _need(sorted_weights, (ms,), torch.float32, "sorted_weights")
+    _need(sorted_expert_ids, (sorted_expert_ids.numel(),), torch.int32, "sorted_expert_ids")
+    if block_m <= 0 or sorted_expert_ids.numel() < ms // block_m:
+        raise ValueError("sorted_expert_ids must hold max_sorted / block_m entries")
+    _need(num_valid, (1,), torch.int32, "num_valid")
+    if fc2_smooth_scale is not None:
+        _need(fc2_smooth_scale, (E, I), torch.float32, "fc2_smooth_scale")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=a8.device)
+    _dev(out, torch.bfloat16, "out")
+    if tuple(out.shape) != (T, H):
+        raise ValueError("out must be [T, H] = %s, got %s" % ((T, H), tuple(out.shape)))
+    if workspace is None:
+        workspace = torch.empty(moe_fp8_blockscale_fused_workspace(T, H, I, E, topk, block_m), dtype=torch.uint8,
+                                device=a8.device)
+    _dev(workspace, torch.uint8, "workspace")
+    ssm, sskb = _scale_strides(a_scale, T, H, scale_layout)
+    _check(lib().moe_fp8_blockscale_fused(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(w1), _ptr(w1_scale), _ptr(w2),
+                                          _ptr(w2_scale), _ptr(sorted_ids), _ptr(sorted_weights),
+                                          _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E, topk, block_m, ms,
+                                          _ptr(fc2_smooth_scale), _ptr(out), _rows(out, "out"), _ptr(workspace),
+                                          workspace.numel(), _stream()))
+    return out
+
+
 # ----------------------------------------------------------------- weight layout
 def shuffle_weight_128x128(w, out=None):
     """e4m3 weights [..., R, K] (R, K multiples of 128) -> the same bytes in the
@@ -357,7 +405,7 @@ class MoELayer:
     """
 
     def __init__(self, cfg, bias, w1, w1_scale, w2, w2_scale, T=None, block_m=None, scale_layout="row",
-                 fc2_smooth_scale=None, preshuffle=False):
+                 fc2_smooth_scale=None, preshuffle=False, fused=False):
         self.cfg = cfg
         self.T = cfg.T if T is None else T
         if block_m is None:
@@ -384,10 +432,19 @@ class MoELayer:
         self.a8 = torch.empty((T, H), dtype=torch.uint8, device=dev)
         self.a_scale = torch.empty((T, H // 128) if scale_layout == "row" else (H // 128, T), dtype=torch.float32,
                                    device=dev)
-        self.h8 = torch.empty((ms, I), dtype=torch.uint8, device=dev)
-        self.h_scale = torch.empty((ms, I // 128), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        self.down_ws = torch.empty(moe_down_combine_workspace(T, H, k), dtype=torch.uint8, device=dev)
+        # fused: the expert computation as one launch (moe_fp8_blockscale_fused), its
+        # intermediates in one workspace; else the two calls on h8 / h_scale / down_ws
+        self.fused = fused
+        if fused:
+            if preshuffle:
+                raise ValueError("the fused call takes weights as loaded (no pre-shuffled variant)")
+            self.fused_ws = torch.empty(moe_fp8_blockscale_fused_workspace(T, H, I, E, k, self.block_m),
+                                        dtype=torch.uint8, device=dev)
+        else:
+            self.h8 = torch.empty((ms, I), dtype=torch.uint8, device=dev)
+            self.h_scale = torch.empty((ms, I // 128), dtype=torch.float32, device=dev)
+            self.down_ws = torch.empty(moe_down_combine_workspace(T, H, k), dtype=torch.uint8, device=dev)
 
     def forward(self, hidden, logits):
         c = self.cfg
@@ -395,6 +452,10 @@ class MoELayer:
                      self.topk_w, self.topk_ids)
         sid, sw, seid, nv = moe_sort(self.topk_ids, self.topk_w, c.E, self.block_m, self.sort_out, self.sort_ws)
         fp8_quant_1x128(hidden, self.a8, self.a_scale, self.scale_layout)
+        if self.fused:
+            return moe_fp8_blockscale_fused(self.a8, self.a_scale, self.w1, self.w1_scale, self.w2, self.w2_scale, sid,
+                                            sw, seid, nv, c.topk, self.block_m, self.out, self.fused_ws,
+                                            self.scale_layout, self.fc2_smooth_scale)
         moe_fp8_blockscale_g1u1(self.a8, self.a_scale, self.w1, self.w1_scale, sid, seid, nv, c.topk, self.block_m,
                                 self.h8, self.h_scale, self.scale_layout, self.fc2_smooth_scale, self.preshuffle)
         moe_down_combine(self.h8, self.h_scale, self.w2, self.w2_scale, sid, sw, seid, nv, self.T, c.topk,

@@ -193,6 +193,33 @@ int moe_down_combine(const uint8_t* h8, const float* h_scale,
                      uint16_t* out, int64_t ld_out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* Host-only workspace query for moe_fp8_blockscale_fused (no GPU access): bytes for the
+ * intermediate h8 [max_sorted, I], its scales [max_sorted, I/128] and the per-pair
+ * fp32 staging [T*topk, H] (max_sorted from moe_sort_sizes for this block_m). */
+int moe_fp8_blockscale_fused_workspace(int T, int H, int I, int E, int topk, int block_m, size_t* bytes);
+
+/*
+ * The whole expert computation in one launch ("Blockscale FP8 MoE Computation": the
+ * pages' fused call takes the sorted buffers to the [tokens, model_dim] output in one
+ * kernel): moe_fp8_blockscale_g1u1 followed by moe_down_combine, run by one cooperative
+ * launch of persistent workgroups with a grid-wide barrier between the gate/up tiles,
+ * the down tiles and the combine.  Arguments are those two calls' (same meaning, same
+ * layouts and rules); h8 / h_scale and the per-pair staging live in `workspace`
+ * (moe_fp8_blockscale_fused_workspace bytes; contents need no initialisation).  Each
+ * tile runs the same arithmetic as the two calls, so `out` equals theirs bit for bit.
+ * block_m in {16, 32, 64, 128} (MOE355_EUNSUPPORTED for 256, or on a device without
+ * cooperative launch).
+ */
+int moe_fp8_blockscale_fused(const uint8_t* a8, const float* a_scale,
+                             int64_t sstride_m, int64_t sstride_kb,
+                             const uint8_t* w1, const float* w1_scale,
+                             const uint8_t* w2, const float* w2_scale,
+                             const int32_t* sorted_ids, const float* sorted_weights,
+                             const int32_t* sorted_expert_ids, const int32_t* num_valid,
+                             int T, int H, int I, int E, int topk, int block_m, int64_t max_sorted,
+                             const float* fc2_smooth_scale, uint16_t* out, int64_t ld_out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Host-only workspace query for gemm_fp8_blockscale (no GPU access): the bytes of
  * fp32 partial sums its split-K path uses for this shape (0 when it does not split). */
 int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes);

@@ -212,6 +212,28 @@ def test_layer_tiny(m, tiny, BM, layout):
     assert_rel_max(f32_of_bf16(out), ref, what="tiny layer")
 
 
+@pytest.mark.parametrize("BM", [16, 32, 64, 128])
+@pytest.mark.parametrize("smooth", [False, True], ids=["plain", "smooth"])
+def test_layer_tiny_fused(m, tiny, BM, smooth):
+    # the single-launch expert computation equals the two calls bit for bit, and the oracle
+    cfg, x = tiny
+    g = {k: v.to(DEV) for k, v in x.items()}
+    sm = None
+    if smooth:
+        sm = torch.from_numpy(np.exp2(np.random.default_rng(BM).uniform(-3, 3, (cfg.E, cfg.I))).astype(np.float32))
+    args = (cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"])
+    kw = dict(block_m=BM, fc2_smooth_scale=None if sm is None else sm.to(DEV))
+    two = m.MoELayer(*args, **kw).forward(g["hidden"], g["logits"]).clone()
+    one = m.MoELayer(*args, fused=True, **kw).forward(g["hidden"], g["logits"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(two.view(torch.int16), one.view(torch.int16))
+    w, ids = oracle_routing(x, cfg)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(x["hidden"]))
+    ref, _, _, _ = oracle.moe.layer_tokens(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), x["w2"].numpy(),
+                                           x["w2_scale"].numpy(), ids, w, None if sm is None else sm.numpy())
+    assert_rel_max(f32_of_bf16(one), ref, what="tiny fused layer")
+
+
 def test_layer_tiny_deterministic(m, tiny):
     cfg, x = tiny
     g = {k: v.to(DEV) for k, v in x.items()}

@@ -139,6 +139,26 @@ def test_layer_all_tokens(m, weights, host_w, name, block_m):
     del layer
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,block_m", [("decode", 16), ("prefill", 128)])
+def test_layer_fused_all_tokens(m, weights, host_w, name, block_m):
+    """The single-launch expert computation at the V3 sizes: equal bit for bit to the
+    two-call layer, and every token within the layer bar of the oracle."""
+    print("layer fused", name, block_m, flush=True)
+    cfg, x, w, ids, _, _, ref, _, _ = _oracle_layer(name, host_w)
+    args = (cfg, x["bias"], weights["w1"], weights["w1_scale"], weights["w2"], weights["w2_scale"])
+    two = m.MoELayer(*args, block_m=block_m)
+    a = two.forward(x["hidden"], x["logits"]).clone()
+    del two
+    one = m.MoELayer(*args, block_m=block_m, fused=True)
+    b = one.forward(x["hidden"], x["logits"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert_rel_max(f32_of_bf16(b), ref, what="%s fused layer (all %d tokens)" % (name, cfg.T))
+    del one
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name,block_m", [("decode", 16), ("prefill", 128)])
 def test_layer_preshuffled_bitwise(m, weights, name, block_m):
     # the whole layer on load-time shuffled V3 weights equals the plain layer bit for bit
