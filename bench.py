@@ -393,11 +393,11 @@ def sweep_block_m(a):
     """Whole-layer time for every M tile over token counts (prefill routing distribution)."""
     base = moe_config("prefill")
     w = None
-    for T in (a.tokens,) if a.tokens else (1, 16, 64, 256, 1024, 4096, 8192):
+    for T in (a.tokens,) if a.tokens else (1, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192):
         cfg = moe_config("prefill", T)
         x = moe_inputs(cfg, a.seed, weights=w)
         w = {k: x[k] for k in ("w1", "w1_scale", "w2", "w2_scale")}
-        for bm in (16, 32, 64, 128):
+        for bm in (16, 32, 64, 128, 256):
             tm = time_layer(cfg, x, bm, a.steps, a.warmup, a.preshuffle, per_call=False)
             print(json.dumps({"sweep": "block_m", "tokens": T, "block_m": bm, "ms": tm["ms"],
                               "median_ms": tm["layer_ms"]["median_ms"], "g1u1_ms": tm["g1u1_ms"],
@@ -411,6 +411,27 @@ V3_LINEAR = [("q_a_proj", 1536, 7168), ("kv_a_proj", 576, 7168), ("q_b_proj", 24
              ("kv_b_proj", 32768, 512), ("o_proj", 7168, 16384), ("dense_mlp_gate_up", 36864, 7168),
              ("dense_mlp_down", 7168, 18432), ("shared_gate_up", 4096, 7168), ("shared_down", 7168, 2048),
              ("config_n2048", 2048, 7168), ("config_n18432", 18432, 7168)]
+
+
+_SLEEP_PER_MS = None
+
+
+def hold_stream(stream, ms):
+    """Queue a spin kernel of about `ms` milliseconds on `stream`, so that the launches the
+    host queues behind it run back to back on the GPU even where one launch takes less
+    time on the GPU than its call on the host."""
+    import torch
+
+    global _SLEEP_PER_MS
+    if _SLEEP_PER_MS is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record(stream)
+        torch.cuda._sleep(1 << 20)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        _SLEEP_PER_MS = (1 << 20) / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(_SLEEP_PER_MS * ms))
 
 
 def time_dense(M, N, K, steps, warmup, seed=0, preshuffle=False):
@@ -448,6 +469,7 @@ def time_dense(M, N, K, steps, warmup, seed=0, preshuffle=False):
     # the GEMM call alone (with its split-K reduce), K launches back to back on the same stream:
     # events around every microsecond-scale launch would mostly time the events
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_stream(stream, 0.1 * steps + 1)
     g0.record(stream)
     for i in range(steps):
         m.gemm_fp8_blockscale(a8, sa, bs[(i + 1) % ncopy], d["b_scale"], c, workspace=ws, preshuffled=preshuffle)
@@ -488,15 +510,71 @@ def bench_dense(a):
             "roofline": roof}
 
 
+SWEEP_M = (1, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
+
+
+def dense_candidates(M, K):
+    """(tile_m, tile_n, splits) tilings the dense sweep times for M rows and K."""
+    KB = -(-K // 128)
+    bms = [16] if M <= 16 else [16, 32] if M <= 32 else [32, 64] if M <= 64 else [64, 128] if M <= 128 else [128]
+    least = -(-KB // 128)  # runs of at most 128 K blocks
+    splits = sorted({max(least, s) for s in ((1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48) if M <= 256 else (1,))
+                     if s == 1 or KB // s >= 2})
+    return [(bm, bn, s) for bm in bms for bn in (128, 256) for s in splits]
+
+
 def sweep_dense(a):
-    """The dense GEMM on every linear-layer shape of a DeepSeek-V3 layer at M 1, 64, 4096."""
+    """Every linear-layer shape of a DeepSeek-V3 layer at M in SWEEP_M: the rule-based plan
+    and each candidate tiling (gemm_fp8_blockscale_tiled) timed back to back over rotated
+    weight copies; one JSON line per (shape, M) with the fastest tiling."""
+    import torch
+
+    import fp8_block_scaled_grouped_amd as m
+    from fp8_block_scaled_grouped_amd import inputs
+
+    dev = torch.device("cuda:0")
+    Ms = (a.tokens,) if a.tokens else SWEEP_M
+    stream = torch.cuda.current_stream()
     for name, N, K in V3_LINEAR:
-        for M in (a.dense_m,) if a.tokens else (1, 64, 4096):
-            t = time_dense(M, N, K, a.steps, a.warmup, a.seed, a.preshuffle)
-            r = dense_roof(M, t)
-            print(json.dumps({"sweep": "dense", "layer": name, "M": M, "N": N, "K": K, "gemm_us": t["gemm_ms"] * 1e3,
-                              "bound": r["bound"], "achieved": r["achieved"], "unit": r["unit"], "frac": r["frac"]}),
+        d = inputs.make_dense_inputs(max(Ms), N, K, dev, seed=a.seed)
+        ncopy = max(1, min(48, (8 << 30) // (N * K)))
+        bs = [d["b"]] + [d["b"].clone() for _ in range(ncopy - 1)]
+        a8_all, sa_all = m.fp8_quant_1x128(d["a"])
+        for M in Ms:
+            a8, sa = a8_all[:M].contiguous(), sa_all[:M].contiguous()
+            c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            reps = 10 if M <= 256 else 4
+
+            def timed(fn):
+                for i in range(2):
+                    fn(bs[i % ncopy])
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                hold_stream(stream, 0.1 * reps + 1)
+                e0.record(stream)
+                for i in range(reps):
+                    fn(bs[(i + 2) % ncopy])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) / reps * 1e3
+
+            nws = m.gemm_fp8_blockscale_workspace(M, N, K)
+            ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+            default_us = timed(lambda b: m.gemm_fp8_blockscale(a8, sa, b, d["b_scale"], c, workspace=ws))
+            plans = []
+            for bm, bn, sp in dense_candidates(M, K):
+                tws = torch.empty(max(m.gemm_fp8_blockscale_tiled_workspace(M, N, K, sp), 16), dtype=torch.uint8,
+                                  device=dev)
+                plans.append([bm, bn, sp, round(timed(lambda b: m.gemm_fp8_blockscale_tiled(
+                    a8, sa, b, d["b_scale"], bm, bn, sp, c, tws)), 3)])
+                del tws
+            best = min(plans, key=lambda p: p[3])
+            flops, nbytes = 2.0 * M * N * K, N * K + M * K + 2 * M * N
+            print(json.dumps({"sweep": "dense", "layer": name, "M": M, "N": N, "K": K, "default_us": round(default_us, 3),
+                              "best": best, "best_tflops": round(flops / best[3] / 1e6, 2),
+                              "best_gbs": round(nbytes / best[3] / 1e3, 1), "plans": plans}),
                   flush=True)
+        del bs, d, a8_all, sa_all
+        torch.cuda.empty_cache()
 
 
 def main():

@@ -36,6 +36,7 @@
 
 #include <hip/hip_cooperative_groups.h>
 
+#include "dense_tuned.h"
 #include "device_common.h"
 #include "gemm_engine.h"
 #include "host_common.h"
@@ -778,7 +779,26 @@ struct DensePlan {
   int bm, bnb, splits, kbs;
 };
 
+// splits -> K blocks per split (kbs) and the split count that covers K with it
+void set_splits(DensePlan& p, int K, int splits) {
+  const int KB = (int)ceil_div64(K, 128);
+  p.kbs = (int)ceil_div64(KB, std::max(1, std::min(splits, KB)));
+  p.splits = (int)ceil_div64(KB, p.kbs);
+}
+
 DensePlan dense_plan(int M, int N, int K) {
+  // measured per-shape plans first (dense_tuned.h): the entry of this N and K whose M
+  // range holds M
+  const DenseTuned* best = nullptr;
+  for (const DenseTuned& t : kDenseTuned)
+    if (best == nullptr && t.n == N && t.k == K && t.m_min <= M && M <= t.m_max) best = &t;
+  if (best != nullptr) {
+    DensePlan p;
+    p.bm = best->bm;
+    p.bnb = best->bnb;
+    set_splits(p, K, std::max(best->splits, (int)ceil_div64(ceil_div64(K, 128), kMaxKbs)));
+    return p;
+  }
   DensePlan p;
   p.bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
   p.bnb = (N % 256 != 0 || (M <= 64 && N <= kNarrowMaxN)) ? 128 : 256;
@@ -858,9 +878,10 @@ extern "C" int moe_fp8_blockscale_fused_workspace(int T, int H, int I, int E, in
 
 namespace {
 
+// forced: a caller-chosen tiling (gemm_fp8_blockscale_tiled), else the tuned / rule-based plan
 int dense_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64_t sstride_kb, const uint8_t* b8,
                const float* b_scale, int M, int N, int K, uint16_t* c, int64_t ldc, int out_fp16, void* workspace,
-               size_t workspace_bytes, hipStream_t stream, bool bsh) {
+               size_t workspace_bytes, hipStream_t stream, bool bsh, const DensePlan* forced = nullptr) {
   MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && ldc >= N && (out_fp16 == 0 || out_fp16 == 1), MOE355_EINVAL);
   MOE355_CHECK(K % 16 == 0 && N % 8 == 0, MOE355_EUNSUPPORTED);
   MOE355_CHECK(!bsh || (K % 128 == 0 && N % 128 == 0), MOE355_EUNSUPPORTED);
@@ -871,9 +892,14 @@ int dense_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64
   MOE355_CHECK((int64_t)M * sstride_m * 4 < (1ll << 32), MOE355_EUNSUPPORTED);
   MOE355_CHECK(aligned16(a8) && aligned16(b8) && aligned16(c) && ldc % 8 == 0, MOE355_EMISALIGNED);
   MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0, MOE355_EMISALIGNED);
-  DensePlan plan = dense_plan(M, N, K);
+  DensePlan plan = forced ? *forced : dense_plan(M, N, K);
   const size_t need = dense_workspace_bytes(plan, M, N);
-  if (need == 0 || workspace == nullptr || workspace_bytes < need) {
+  if (forced != nullptr) {
+    // a caller-chosen plan runs as given: its split of K needs the workspace
+    MOE355_CHECK(plan.kbs <= kMaxKbs, MOE355_EUNSUPPORTED);
+    MOE355_CHECK(need == 0 || (workspace != nullptr && workspace_bytes >= need), MOE355_EINVAL);
+    MOE355_CHECK(need == 0 || aligned16(workspace), MOE355_EMISALIGNED);
+  } else if (need == 0 || workspace == nullptr || workspace_bytes < need) {
     // without (enough) workspace: one workgroup per output tile walks all of K, which
     // holds the weight scales of at most kMaxKbs K blocks
     MOE355_CHECK(ceil_div64(K, 128) <= kMaxKbs, need > 0 && workspace != nullptr ? MOE355_EINVAL : MOE355_EUNSUPPORTED);
@@ -1029,6 +1055,29 @@ extern "C" int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale, int6
                                    hipStream_t stream) {
   return dense_gemm(a8, a_scale, sstride_m, sstride_kb, b8, b_scale, M, N, K, c, ldc, out_fp16, workspace,
                     workspace_bytes, stream, false);
+}
+
+extern "C" int gemm_fp8_blockscale_tiled(const uint8_t* a8, const float* a_scale, int64_t sstride_m,
+                                         int64_t sstride_kb, const uint8_t* b8, const float* b_scale, int M, int N,
+                                         int K, uint16_t* c, int64_t ldc, int out_fp16, int tile_m, int tile_n,
+                                         int splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  MOE355_CHECK(splits >= 1, MOE355_EINVAL);
+  MOE355_CHECK((tile_m == 16 || tile_m == 32 || tile_m == 64 || tile_m == 128) && (tile_n == 128 || tile_n == 256),
+               MOE355_EUNSUPPORTED);
+  DensePlan p;
+  p.bm = tile_m;
+  p.bnb = tile_n;
+  set_splits(p, K, splits);
+  return dense_gemm(a8, a_scale, sstride_m, sstride_kb, b8, b_scale, M, N, K, c, ldc, out_fp16, workspace,
+                    workspace_bytes, stream, false, &p);
+}
+
+extern "C" int gemm_fp8_blockscale_tiled_workspace(int M, int N, int K, int splits, size_t* bytes) {
+  MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && splits >= 1 && bytes, MOE355_EINVAL);
+  DensePlan p{16, 128, 1, 1};
+  set_splits(p, K, splits);
+  *bytes = (M == 0 || N == 0 || K == 0) ? 0 : dense_workspace_bytes(p, M, N);
+  return MOE355_OK;
 }
 
 extern "C" int gemm_fp8_blockscale_wpreshuffle(const uint8_t* a8, const float* a_scale, int64_t sstride_m,

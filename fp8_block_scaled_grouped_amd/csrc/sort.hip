@@ -12,6 +12,7 @@
 // The result is the unique stable order: experts ascending, pairs ascending.
 #include "device_common.h"
 #include "host_common.h"
+#include "block_m_tuned.h"
 
 namespace moe355 {
 namespace {
@@ -279,6 +280,17 @@ extern "C" int moe_sort_sizes(int T, int topk, int E, int block_m, int64_t* max_
 extern "C" int moe_block_m(int T, int topk, int E, int* block_m) {
   MOE355_CHECK(T >= 0 && topk > 0 && E > 0 && block_m, MOE355_EINVAL);
   const int64_t pairs = (int64_t)T * topk;
+  // measured table (block_m_tuned.h) by mean pairs per expert, else the rule: 16-row tiles
+  // while experts average under 4 pairs, 32 under 16, 128 above
+  const int n = (int)(sizeof(kBlockMTuned) / sizeof(kBlockMTuned[0]));
+  if (kBlockMTuned[0].block_m > 0) {
+    const double ppe = (double)pairs / E;
+    int bm = kBlockMTuned[n - 1].block_m;
+    for (int i = n - 1; i >= 0; --i)
+      if (ppe <= kBlockMTuned[i].ppe_max) bm = kBlockMTuned[i].block_m;
+    *block_m = bm;
+    return MOE355_OK;
+  }
   *block_m = pairs < 4ll * E ? 16 : pairs < 16ll * E ? 32 : 128;
   return MOE355_OK;
 }

@@ -37,6 +37,9 @@ _SIGNATURES = {
     "shuffle_weight_128x128": ([_vp, _i64, _i32, _vp, _vp], _i32),
     "gemm_fp8_blockscale_noalloc": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _vp], _i32),
     "moe_fp8_blockscale_fused_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, _PSZ], _i32),
+    "gemm_fp8_blockscale_tiled": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _i32, _i32, _i32,
+                                   _vp, _sz, _vp], _i32),
+    "gemm_fp8_blockscale_tiled_workspace": ([_i32, _i32, _i32, _i32, _PSZ], _i32),
     "moe_fp8_blockscale_fused": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _i64, _vp, _vp, _i64, _vp, _sz, _vp], _i32),
 }
@@ -293,6 +296,37 @@ def moe_down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sort
               _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E, topk, block_m, ms, _ptr(out), _rows(out, "out"),
               _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+def gemm_fp8_blockscale_tiled_workspace(M, N, K, splits):
+    b = ctypes.c_size_t()
+    _check(lib().gemm_fp8_blockscale_tiled_workspace(M, N, K, splits, ctypes.byref(b)))
+    return b.value
+
+
+def gemm_fp8_blockscale_tiled(a8, a_scale, b8, b_scale, tile_m, tile_n, splits, c=None, workspace=None,
+                              scale_layout="row", out_dtype=torch.bfloat16):
+    """gemm_fp8_blockscale with a caller-chosen tiling (tile_m rows x tile_n columns, K in
+    `splits` runs); workspace None allocates what the split needs."""
+    M, K = a8.shape
+    N = b8.shape[0]
+    _need(a8, (M, K), torch.uint8, "a8")
+    _need(b8, (N, K), torch.uint8, "b8")
+    _need(b_scale, (_nblk(N), _nblk(K)), torch.float32, "b_scale")
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a8.device)
+    if c.dtype not in (torch.bfloat16, torch.float16) or tuple(c.shape) != (M, N):
+        raise ValueError("c must be bf16 or fp16 [M, N]")
+    _dev(c, c.dtype, "c")
+    if workspace is None:
+        n = gemm_fp8_blockscale_tiled_workspace(M, N, K, splits)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=a8.device)
+    _dev(workspace, torch.uint8, "workspace")
+    ssm, sskb = _scale_strides(a_scale, M, K, scale_layout)
+    _check(lib().gemm_fp8_blockscale_tiled(_ptr(a8), _ptr(a_scale), ssm, sskb, _ptr(b8), _ptr(b_scale), M, N, K,
+                                           _ptr(c), _rows(c, "c"), int(c.dtype == torch.float16), tile_m, tile_n,
+                                           splits, _ptr(workspace), workspace.numel(), _stream()))
+    return c
 
 
 def moe_fp8_blockscale_fused_workspace(T, H, I, E, topk, block_m):

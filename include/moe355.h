@@ -253,6 +253,26 @@ int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale,
                         hipStream_t stream);
 
 /*
+ * gemm_fp8_blockscale with the tiling chosen by the caller ("General Linear Layer": the
+ * pages pick the GEMM per DeepSeek-V3/R1 shape from a tuned table; this call is what a
+ * sweep times to build one): output tiles of tile_m rows (16, 32, 64 or 128) by tile_n
+ * columns (128 or 256), and K split into `splits` runs of whole 128-wide blocks whose
+ * fp32 partial sums are added in a fixed order.  splits > 1 needs a workspace of
+ * gemm_fp8_blockscale_tiled_workspace() bytes (MOE355_EINVAL without it); a run of more
+ * than 128 K blocks is MOE355_EUNSUPPORTED.  Arguments, results and other errors are
+ * those of gemm_fp8_blockscale (the arithmetic per output element is the same, whatever
+ * the tiling; only the order of the split sums can differ).
+ */
+int gemm_fp8_blockscale_tiled(const uint8_t* a8, const float* a_scale,
+                              int64_t sstride_m, int64_t sstride_kb,
+                              const uint8_t* b8, const float* b_scale,
+                              int M, int N, int K, uint16_t* c, int64_t ldc, int out_fp16,
+                              int tile_m, int tile_n, int splits,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* Host-only: the workspace gemm_fp8_blockscale_tiled needs for this shape and split count. */
+int gemm_fp8_blockscale_tiled_workspace(int M, int N, int K, int splits, size_t* bytes);
+
+/*
  * gemm_fp8_blockscale for callers that cannot allocate device memory (code under
  * HIP-graph capture, tight serving loops, harnesses that forbid allocation): the
  * same arguments, results and errors as gemm_fp8_blockscale with its workspace,

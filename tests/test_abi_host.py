@@ -156,12 +156,28 @@ def test_zero_rows_are_noops_without_touching_memory(lib):
 
 
 def test_block_m_table(lib):
+    import json
+    import os
+
     from fp8_block_scaled_grouped_amd import moe355
-    # V3 (E 256, top-8): decode-sized batches stream weights with 16-row tiles,
-    # a few hundred tokens use 32, prefill sizes the 128-row tile
-    assert [moe355.moe_block_m(T, 8, 256) for T in (1, 64, 127, 128, 256, 511, 512, 8192)] == \
-        [16, 16, 16, 32, 32, 32, 128, 128]
-    assert moe355.moe_block_m(0, 8, 256) == 16
+    # the compiled table returns, at every swept token count of the V3 layer (E 256,
+    # top-8), the M tile whose whole-layer time was smallest in the committed sweep, and
+    # between two swept counts the choice of the larger one
+    path = os.path.join(os.path.dirname(moe355.__file__), "tuning", "block_m_sweep.jsonl")
+    best = {}
+    for line in open(path):
+        r = json.loads(line)
+        if r.get("sweep") == "block_m" and (r["tokens"] not in best or r["ms"] < best[r["tokens"]][1]):
+            best[r["tokens"]] = (r["block_m"], r["ms"])
+    Ts = sorted(best)
+    assert len(Ts) >= 8
+    for i, T in enumerate(Ts):
+        assert moe355.moe_block_m(T, 8, 256) == best[T][0], T
+        if i > 0 and T - Ts[i - 1] > 1:
+            assert moe355.moe_block_m(Ts[i - 1] + 1, 8, 256) == best[T][0], T
+    # beyond the sweep: the largest count's tile; no tokens: the smallest count's tile
+    assert moe355.moe_block_m(4 * Ts[-1], 8, 256) == best[Ts[-1]][0]
+    assert moe355.moe_block_m(0, 8, 256) == best[Ts[0]][0]
     with pytest.raises(moe355.Moe355Error):
         moe355.moe_block_m(1, 0, 256)
 

@@ -518,3 +518,55 @@ def test_layer_seeds_all_stages(m, seed):
     pos = {int(p): r for r, p in enumerate(rsid) if p < T * cfg.topk}
     rows = [pos[t * cfg.topk + j] for t in range(T) for j in range(cfg.topk)]
     check_requant(np_u8(layer.h8)[rows], layer.h_scale.cpu().numpy()[rows], h_ref.reshape(-1, cfg.I))
+
+
+# caller-chosen tilings: every tile_m x tile_n with the same K split gives the same bits
+# (each output element sums the same K blocks in the same order, whichever workgroup holds
+# it), the plan gemm_fp8_blockscale picks among them; all within the oracle's tolerance.
+# Shapes: ragged M and N (N off a multiple of 256 and of 128), partial K, long K
+@pytest.mark.parametrize("M,N,K", [(70, 1040, 1536), (5, 2048, 7168), (130, 520, 1040), (3, 576, 16512)])
+def test_dense_tiled_plans(m, M, N, K):
+    from fp8_block_scaled_grouped_amd import inputs
+    print("dense tiled", M, N, K, flush=True)
+    d = inputs.make_dense_inputs(M, N, K, "cpu", seed=M + 11 * N + K)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(d["a"]))
+    ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
+    args = (torch.from_numpy(a8).to(DEV), torch.from_numpy(sa).to(DEV), d["b"].to(DEV), d["b_scale"].to(DEV))
+    KB = -(-K // 128)
+    least = -(-KB // 128)
+    outs = {}
+    for sp in sorted({max(least, s) for s in (1, 3, 8)}):
+        for bm in (16, 32, 64, 128):
+            for bn in (128, 256):
+                ws = torch.full((max(m.gemm_fp8_blockscale_tiled_workspace(M, N, K, sp), 16),), 0x7F,
+                                dtype=torch.uint8, device=DEV)
+                c = m.gemm_fp8_blockscale_tiled(*args, bm, bn, sp, workspace=ws)
+                torch.cuda.synchronize()
+                outs[(bm, bn, sp)] = c.view(torch.int16).cpu()
+        first = outs[(16, 128, sp)]
+        for key, v in outs.items():
+            if key[2] == sp:
+                assert torch.equal(v, first), key
+        assert_rel_max(f32_of_bf16(first.view(torch.bfloat16)), ref, what="tiled splits %d" % sp)
+    # the default plan's K split (read back from its workspace size), run as a tiling, gives
+    # the default call's bits
+    nws = m.gemm_fp8_blockscale_workspace(M, N, K)
+    sp = (nws - 256) // (M * N * 4) if nws else 1
+    c = m.gemm_fp8_blockscale(*args)
+    t = m.gemm_fp8_blockscale_tiled(*args, 64, 256, sp)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), t.view(torch.int16)), sp
+
+
+def test_dense_tiled_rejects(m):
+    from fp8_block_scaled_grouped_amd import inputs
+    d = inputs.make_dense_inputs(8, 256, 16512, DEV, seed=1)
+    a8, sa = m.fp8_quant_1x128(d["a"])
+    with pytest.raises(RuntimeError):  # K of 129 blocks in one run: beyond the scales a workgroup holds
+        m.gemm_fp8_blockscale_tiled(a8, sa, d["b"], d["b_scale"], 16, 128, 1)
+    with pytest.raises(RuntimeError):  # tile shape outside the compiled set
+        m.gemm_fp8_blockscale_tiled(a8, sa, d["b"], d["b_scale"], 48, 128, 2)
+    with pytest.raises(RuntimeError):  # a split without workspace
+        m.gemm_fp8_blockscale_tiled(a8, sa, d["b"], d["b_scale"], 16, 128, 2,
+                                    workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()

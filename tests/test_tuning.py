@@ -1,0 +1,80 @@
+"""Host-side checks of the plan-table generator and of the tables compiled in."""
+import json
+import os
+import subprocess
+import sys
+
+from fp8_block_scaled_grouped_amd.tuning import make_tables as mt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _rec(M, N, K, default_us, plans):
+    return {"sweep": "dense", "layer": "x", "M": M, "N": N, "K": K, "default_us": default_us, "plans": plans}
+
+
+def test_dense_rows_margin_ranges_and_scratch_cap():
+    recs = [
+        _rec(1, 2048, 7168, 10.0, [[16, 128, 8, 9.0], [16, 256, 16, 9.5]]),  # 10% faster: kept
+        _rec(16, 2048, 7168, 10.0, [[16, 128, 8, 9.9]]),  # within the margin: rule stays
+        _rec(64, 2048, 7168, 20.0, [[32, 128, 4, 15.0]]),
+        # a split whose partials exceed the static scratch is skipped for the next best
+        _rec(256, 18432, 7168, 100.0, [[128, 256, 4, 50.0], [128, 256, 1, 80.0]]),
+    ]
+    rows = mt.dense_rows(recs)
+    assert [(r[0], r[1], r[2], r[3], r[4], r[5], r[6]) for r in rows] == [
+        (1, 1, 2048, 7168, 16, 128, 8), (17, 64, 2048, 7168, 32, 128, 4), (1, 256, 18432, 7168, 128, 256, 1)]
+
+
+def test_kb_per_split_matches_the_library_rule():
+    # 56 K blocks in 24 runs -> runs of 3 blocks, 19 of them; one run when K fits
+    assert mt.kb_per_split(7168, 24) == (3, 19)
+    assert mt.kb_per_split(7168, 1) == (56, 1)
+    assert mt.kb_per_split(1040, 100) == (1, 9)
+
+
+def test_block_m_rows_pick_fastest_and_merge():
+    recs = []
+    for T, times in [(1, {16: 1.0, 32: 1.1}), (8, {16: 1.0, 32: 1.2}), (256, {16: 3.0, 32: 2.0}),
+                     (8192, {32: 9.0, 128: 8.0})]:
+        for bm, ms in times.items():
+            recs.append({"sweep": "block_m", "tokens": T, "block_m": bm, "ms": ms, "topk": 8, "experts": 256})
+    rows = mt.block_m_rows(recs)
+    assert [(r[0], r[1]) for r in rows] == [(8 * 8 / 256, 16), (256 * 8 / 256, 32), (8192 * 8 / 256, 128)]
+
+
+def test_written_headers_parse_back(tmp_path):
+    mt.write_dense([(1, 64, 2048, 7168, 16, 128, 8, 9.0, 10.0)], "t", str(tmp_path))
+    mt.write_block_m([(2.0, 16, 1.0, {16: 1.0})], "t", str(tmp_path))
+    d = (tmp_path / "dense_tuned.h").read_text()
+    assert "{1, 64, 2048, 7168, 16, 128, 8}" in d
+    b = (tmp_path / "block_m_tuned.h").read_text()
+    assert "{2, 16}" in b
+
+
+def test_committed_tables_are_the_generators_output(tmp_path):
+    # the headers in csrc/ are what make_tables writes from the committed sweep records
+    tdir = os.path.join(ROOT, "fp8_block_scaled_grouped_amd", "tuning")
+    csrc = os.path.join(ROOT, "fp8_block_scaled_grouped_amd", "csrc")
+    subprocess.check_call([sys.executable, "-m", "fp8_block_scaled_grouped_amd.tuning.make_tables", "--out-dir",
+                           str(tmp_path)], cwd=ROOT)
+    for name, sweep in (("dense_tuned.h", "dense_sweep.jsonl"), ("block_m_tuned.h", "block_m_sweep.jsonl")):
+        if os.path.exists(os.path.join(tdir, sweep)):
+            with open(os.path.join(csrc, name)) as f:
+                assert (tmp_path / name).read_text() == f.read(), name
+
+
+def test_library_plans_follow_the_dense_table():
+    # where the table holds a tiling, the workspace the library asks for at both ends of
+    # the entry's M range is that tiling's split-K partials; elsewhere the rule's
+    from fp8_block_scaled_grouped_amd import moe355
+    path = os.path.join(ROOT, "fp8_block_scaled_grouped_amd", "tuning", "dense_sweep.jsonl")
+    if not os.path.exists(path):
+        return
+    rows = mt.dense_rows(mt.read(path, "dense"))
+    assert rows
+    for m0, m1, n, k, bm, bnb, sp, us, dus in rows:
+        runs = mt.kb_per_split(k, sp)[1]
+        for M in (m0, m1):
+            want = runs * M * n * 4 + 256 if runs > 1 else 0
+            assert moe355.gemm_fp8_blockscale_workspace(M, n, k) == want, (M, n, k, sp)
