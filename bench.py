@@ -62,15 +62,9 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ["fp8_block_scaled_grouped_amd/csrc/gemm.hip", "fp8_block_scaled_grouped_amd/csrc/device_common.h"]
-
-
 def kernel_source_hash():
-    import hashlib
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    return h.hexdigest()[:16]
+    from fp8_block_scaled_grouped_amd.tuning.rocprof_summary import source_hash
+    return source_hash()
 
 
 def measured_traffic(workload, kernel):

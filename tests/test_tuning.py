@@ -78,3 +78,29 @@ def test_library_plans_follow_the_dense_table():
         for M in (m0, m1):
             want = runs * M * n * 4 + 256 if runs > 1 else 0
             assert moe355.gemm_fp8_blockscale_workspace(M, n, k) == want, (M, n, k, sp)
+
+
+def test_rocprof_summary_roles_and_traffic_scaling(tmp_path):
+    from fp8_block_scaled_grouped_amd.tuning import rocprof_summary as rs
+    g1u1 = "void moe355::(anonymous namespace)::bs_gemm_kernel<moe355::(anonymous namespace)::Cfg<1, 128, 256, 8, 2, 3>, 1, false, false>(moe355::GemmArgs)"
+    assert rs.role(g1u1) == ("g1u1", "g1u1 (BM 128, B rows 256, 8 waves, 3 stages)")
+    assert rs.role("big_gemm_kernel<2, false>")[0] == "down"
+    assert rs.role("__amd_rocclr_copyBuffer")[0] == "copy"
+    assert rs.role("at::native::elementwise_kernel<...>")[0] is None
+    # counters: two g1u1 dispatches and three calibration copies; bytes = KiB * copy bytes / copy KiB
+    for counter, kib, copy_kib in (("FETCH_SIZE", (100.0, 300.0), 512.0), ("WRITE_SIZE", (10.0, 30.0), 1024.0)):
+        d = tmp_path / counter / "host" / "1"
+        d.mkdir(parents=True)
+        lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        lines += ['%d,"%s",%s,%f' % (i, g1u1, counter, v) for i, v in enumerate(kib)]
+        lines += ["%d,__amd_rocclr_copyBuffer,%s,%f" % (10 + i, counter, copy_kib) for i in range(3)]
+        (d / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+    out = tmp_path / "t.json"
+    subprocess.check_call([sys.executable, "-m", "fp8_block_scaled_grouped_amd.tuning.rocprof_summary", "traffic",
+                           "--fetch-dir", str(tmp_path / "FETCH_SIZE"), "--write-dir", str(tmp_path / "WRITE_SIZE"),
+                           "--workload", "w", "--copy-bytes", str(1 << 20), "--command-fetch", "f",
+                           "--command-write", "w", "--out", str(out)], cwd=ROOT)
+    k = json.loads(out.read_text())["kernels"]["g1u1"]
+    assert k["fetch_bytes"] == 200.0 * (1 << 20) / 512.0
+    assert k["write_bytes"] == 20.0 * (1 << 20) / 1024.0
+    assert k["dispatches"] == 2
