@@ -87,9 +87,11 @@ int moe_sort_sizes(int T, int topk, int E, int block_m,
 
 /*
  * Host-only tile choice for moe_sort and the grouped GEMMs (no GPU access): the
- * block_m that measured fastest for the whole layer at this size, from the expected
- * pairs per expert p = T*topk/E:  p < 4 -> 16;  p < 16 -> 32;  else 128.
- * Routing that concentrates pairs on few experts favours a larger block_m than this.
+ * block_m whose whole DeepSeek-V3 layer measured fastest at this size, looked up by
+ * the mean pairs per expert p = T*topk/E in a table compiled into the library
+ * (generated from a committed sweep; for that sweep: p <= 2 -> 16, p <= 4 -> 32,
+ * p <= 16 -> 64, else 128).  Routing that concentrates pairs on few experts favours a
+ * larger block_m than this.
  */
 int moe_block_m(int T, int topk, int E, int* block_m);
 
@@ -239,7 +241,9 @@ int gemm_fp8_blockscale_workspace(int M, int N, int K, size_t* bytes);
  * workspace device memory of gemm_fp8_blockscale_workspace() bytes, or NULL / 0: small M
  *          then splits K over more workgroups, keeps fp32 partial sums there and adds them
  *          in a fixed order (deterministic); without it one workgroup per output
- *          tile walks all of K.  Contents need no initialisation.  K above 16384 (more
+ *          tile walks all of K.  The tiling (and so the workspace size) comes from a
+ *          table of measured plans for the DeepSeek-V3 linear-layer shapes compiled into
+ *          the library, else from a rule on M, N and K.  Contents need no initialisation.  K above 16384 (more
  *          than 128 K blocks) is always split and needs the workspace: without it
  *          MOE355_EUNSUPPORTED, with too little MOE355_EINVAL.
  * K % 16 == 0, N % 8 == 0 and M * sstride_m * 4 < 2^32 (else MOE355_EUNSUPPORTED);

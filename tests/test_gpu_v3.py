@@ -39,14 +39,14 @@ def weights():
 
 def _inputs(name, T=None):
     from fp8_block_scaled_grouped_amd import inputs
-    cfg = inputs.MOE_CONFIGS[name]
+    cfg = {**inputs.MOE_CONFIGS, **inputs.CONTROL_CONFIGS}[name]
     if T is not None:
         cfg = inputs.with_tokens(cfg, T)
     x = inputs.make_moe_inputs(cfg, DEV, seed=0, weights=False)
     return cfg, x
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "skew"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "skew_zipf", "prefill_bias0"])
 def test_routing_and_sort_bitexact(m, name):
     cfg, x = _inputs(name)
     print("routing/sort", name, flush=True)
@@ -113,7 +113,10 @@ def host_w(weights):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,block_m", [("decode", 16), ("decode", 32), ("decode", 128), ("prefill", 128),
                                           ("prefill", 64), ("prefill", 256), ("skew", 128), ("skew", 64),
-                                          ("skew", 256)])
+                                          ("skew", 256),
+                                          # the routing controls: Zipf popularity without the hot bias
+                                          # (255 experts, a long tail of small loads), and zero bias
+                                          ("skew_zipf", 128), ("skew_zipf", 32), ("prefill_bias0", 128)])
 def test_layer_all_tokens(m, weights, host_w, name, block_m):
     """The whole layer against the oracle on every token: the bf16 output of all T tokens
     (max|gpu - ref| <= 1e-2 max|ref|) and the requantised h of every routed pair."""
