@@ -453,6 +453,7 @@ def time_dense(M, N, K, steps, warmup, seed=0, preshuffle=False):
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    hold_stream(stream, 0.1 * steps + 1)  # the steps run back to back on the GPU
     start.record(stream)
     for i in range(steps):
         m.fp8_quant_1x128(d["a"], a8, sa)
@@ -514,13 +515,17 @@ def dense_candidates(M, K):
     least = -(-KB // 128)  # runs of at most 128 K blocks
     splits = sorted({max(least, s) for s in ((1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48) if M <= 256 else (1,))
                      if s == 1 or KB // s >= 2})
-    return [(bm, bn, s) for bm in bms for bn in (128, 256) for s in splits]
+    plans = [(bm, bn, s) for bm in bms for bn in (128, 256) for s in splits]
+    if M <= 64:  # the small-M kernel: 16-column tiles, K split inside the workgroup
+        plans.append((16 if M <= 16 else 32 if M <= 32 else 64, 16, 1))
+    return plans
 
 
 def sweep_dense(a):
-    """Every linear-layer shape of a DeepSeek-V3 layer at M in SWEEP_M: the rule-based plan
-    and each candidate tiling (gemm_fp8_blockscale_tiled) timed back to back over rotated
-    weight copies; one JSON line per (shape, M) with the fastest tiling."""
+    """Every linear-layer shape of a DeepSeek-V3 layer at M in SWEEP_M: the call as it
+    stands (default_us), the rule's plan alone (rule) and each candidate tiling
+    (gemm_fp8_blockscale_tiled), timed back to back over rotated weight copies; one JSON
+    line per (shape, M) with every timing."""
     import torch
 
     import fp8_block_scaled_grouped_amd as m
@@ -561,10 +566,17 @@ def sweep_dense(a):
                 plans.append([bm, bn, sp, round(timed(lambda b: m.gemm_fp8_blockscale_tiled(
                     a8, sa, b, d["b_scale"], bm, bn, sp, c, tws)), 3)])
                 del tws
+            # the rule's plan (what the table's entries must beat), timed as a tiling
+            rtm, rtn, rsp = m.gemm_fp8_blockscale_plan(M, N, K, measured=False)
+            tws = torch.empty(max(m.gemm_fp8_blockscale_tiled_workspace(M, N, K, rsp), 16), dtype=torch.uint8,
+                              device=dev)
+            rule = [rtm, rtn, rsp, round(timed(lambda b: m.gemm_fp8_blockscale_tiled(
+                a8, sa, b, d["b_scale"], rtm, rtn, rsp, c, tws)), 3)]
+            del tws
             best = min(plans, key=lambda p: p[3])
             flops, nbytes = 2.0 * M * N * K, N * K + M * K + 2 * M * N
             print(json.dumps({"sweep": "dense", "layer": name, "M": M, "N": N, "K": K, "default_us": round(default_us, 3),
-                              "best": best, "best_tflops": round(flops / best[3] / 1e6, 2),
+                              "rule": rule, "best": best, "best_tflops": round(flops / best[3] / 1e6, 2),
                               "best_gbs": round(nbytes / best[3] / 1e3, 1), "plans": plans}),
                   flush=True)
         del bs, d, a8_all, sa_all

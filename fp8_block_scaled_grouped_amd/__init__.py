@@ -10,6 +10,7 @@ from .moe355 import (  # noqa: F401
     Moe355Error,
     fp8_quant_1x128,
     gemm_fp8_blockscale,
+    gemm_fp8_blockscale_plan,
     gemm_fp8_blockscale_tiled,
     gemm_fp8_blockscale_tiled_workspace,
     gemm_fp8_blockscale_workspace,

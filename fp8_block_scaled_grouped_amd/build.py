@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe355.so")
-SOURCES = ["gemm.hip", "gemm_big.hip", "topk.hip", "sort.hip", "quant.hip", "shuffle.hip", "status.cpp"]
+SOURCES = ["gemm.hip", "gemm_big.hip", "dense_small.hip", "topk.hip", "sort.hip", "quant.hip", "shuffle.hip", "status.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # per-source extra flags: MFMA results in VGPRs so the fp32 fold reads them directly

@@ -36,6 +36,7 @@
 
 #include <hip/hip_cooperative_groups.h>
 
+#include "dense_small.h"
 #include "dense_tuned.h"
 #include "device_common.h"
 #include "gemm_engine.h"
@@ -786,6 +787,8 @@ void set_splits(DensePlan& p, int K, int splits) {
   p.splits = (int)ceil_div64(KB, p.kbs);
 }
 
+DensePlan dense_rule_plan(int M, int N, int K);
+
 DensePlan dense_plan(int M, int N, int K) {
   // measured per-shape plans first (dense_tuned.h): the entry of this N and K whose M
   // range holds M
@@ -796,9 +799,15 @@ DensePlan dense_plan(int M, int N, int K) {
     DensePlan p;
     p.bm = best->bm;
     p.bnb = best->bnb;
-    set_splits(p, K, std::max(best->splits, (int)ceil_div64(ceil_div64(K, 128), kMaxKbs)));
+    // 16-column tiles split K inside the workgroup (no run limit); the others walk at
+    // most kMaxKbs K blocks per run
+    set_splits(p, K, best->bnb == 16 ? 1 : std::max(best->splits, (int)ceil_div64(ceil_div64(K, 128), kMaxKbs)));
     return p;
   }
+  return dense_rule_plan(M, N, K);
+}
+
+DensePlan dense_rule_plan(int M, int N, int K) {
   DensePlan p;
   p.bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
   p.bnb = (N % 256 != 0 || (M <= 64 && N <= kNarrowMaxN)) ? 128 : 256;
@@ -893,6 +902,24 @@ int dense_gemm(const uint8_t* a8, const float* a_scale, int64_t sstride_m, int64
   MOE355_CHECK(aligned16(a8) && aligned16(b8) && aligned16(c) && ldc % 8 == 0, MOE355_EMISALIGNED);
   MOE355_CHECK((reinterpret_cast<uintptr_t>(a_scale) & 3u) == 0, MOE355_EMISALIGNED);
   DensePlan plan = forced ? *forced : dense_plan(M, N, K);
+  if (plan.bnb == 16) {
+    // small M: one workgroup per 16 columns, K split over its waves (dense_small.hip)
+    MOE355_CHECK(M <= 64 && plan.splits == 1, MOE355_EUNSUPPORTED);
+    DenseSmallArgs s{};
+    s.a = a8;
+    s.a_scale = a_scale;
+    s.ssm = sstride_m;
+    s.sskb = sstride_kb;
+    s.b = b8;
+    s.b_scale = b_scale;
+    s.M = M;
+    s.N = N;
+    s.K = K;
+    s.c = c;
+    s.ldc = ldc;
+    s.out_f16 = out_fp16;
+    return launch_dense_small(s, bsh, stream);
+  }
   const size_t need = dense_workspace_bytes(plan, M, N);
   if (forced != nullptr) {
     // a caller-chosen plan runs as given: its split of K needs the workspace
@@ -1062,14 +1089,27 @@ extern "C" int gemm_fp8_blockscale_tiled(const uint8_t* a8, const float* a_scale
                                          int K, uint16_t* c, int64_t ldc, int out_fp16, int tile_m, int tile_n,
                                          int splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   MOE355_CHECK(splits >= 1, MOE355_EINVAL);
-  MOE355_CHECK((tile_m == 16 || tile_m == 32 || tile_m == 64 || tile_m == 128) && (tile_n == 128 || tile_n == 256),
+  MOE355_CHECK((tile_m == 16 || tile_m == 32 || tile_m == 64 || tile_m == 128) &&
+                   (tile_n == 16 || tile_n == 128 || tile_n == 256),
                MOE355_EUNSUPPORTED);
+  // 16-column tiles: the small-M kernel (M <= 64, K split inside the workgroup)
+  MOE355_CHECK(tile_n != 16 || (tile_m <= 64 && M <= tile_m && splits == 1), MOE355_EUNSUPPORTED);
   DensePlan p;
   p.bm = tile_m;
   p.bnb = tile_n;
   set_splits(p, K, splits);
   return dense_gemm(a8, a_scale, sstride_m, sstride_kb, b8, b_scale, M, N, K, c, ldc, out_fp16, workspace,
                     workspace_bytes, stream, false, &p);
+}
+
+extern "C" int gemm_fp8_blockscale_plan(int M, int N, int K, int measured, int* tile_m, int* tile_n, int* splits) {
+  MOE355_CHECK(M >= 0 && N >= 0 && K >= 0 && tile_m && tile_n && splits, MOE355_EINVAL);
+  MOE355_CHECK(K % 16 == 0 && N % 8 == 0, MOE355_EUNSUPPORTED);
+  const DensePlan p = measured ? dense_plan(M, N, K) : dense_rule_plan(M, N, K);
+  *tile_m = p.bm;
+  *tile_n = p.bnb;
+  *splits = p.splits;
+  return MOE355_OK;
 }
 
 extern "C" int gemm_fp8_blockscale_tiled_workspace(int M, int N, int K, int splits, size_t* bytes) {

@@ -40,6 +40,8 @@ _SIGNATURES = {
     "gemm_fp8_blockscale_tiled": ([_vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _i64, _i32, _i32, _i32, _i32,
                                    _vp, _sz, _vp], _i32),
     "gemm_fp8_blockscale_tiled_workspace": ([_i32, _i32, _i32, _i32, _PSZ], _i32),
+    "gemm_fp8_blockscale_plan": ([_i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                  ctypes.POINTER(ctypes.c_int)], _i32),
     "moe_fp8_blockscale_fused": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                   _i32, _i32, _i64, _vp, _vp, _i64, _vp, _sz, _vp], _i32),
 }
@@ -296,6 +298,15 @@ def moe_down_combine(h8, h_scale, w2, w2_scale, sorted_ids, sorted_weights, sort
               _ptr(sorted_expert_ids), _ptr(num_valid), T, H, I, E, topk, block_m, ms, _ptr(out), _rows(out, "out"),
               _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+def gemm_fp8_blockscale_plan(M, N, K, measured=True):
+    """(tile_m, tile_n, splits) gemm_fp8_blockscale runs for this shape (host-only);
+    measured=False: the rule alone, without the table of measured plans."""
+    tm, tn, sp = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().gemm_fp8_blockscale_plan(M, N, K, int(bool(measured)), ctypes.byref(tm), ctypes.byref(tn),
+                                          ctypes.byref(sp)))
+    return tm.value, tn.value, sp.value
 
 
 def gemm_fp8_blockscale_tiled_workspace(M, N, K, splits):

@@ -6,8 +6,9 @@
     python -c "import __graft_entry__ as g; g.build()"
 
 csrc/dense_tuned.h: per (N, K) and M range, the tiling (tile_m, tile_n, K splits) that
-timed fastest, where it beat the rule-based plan by more than MARGIN; other M ranges keep
-the rule.  A split is kept only while its fp32 partials fit the static scratch of the
+timed fastest, where it beat the rule's own plan (timed in the same sweep, so the table
+does not depend on the table it replaces) by more than MARGIN; other M ranges keep
+the rule.  tile_n 16 is the small-M kernel (K split inside the workgroup, no workspace).  A split is kept only while its fp32 partials fit the static scratch of the
 allocation-free entry point, so that entry point runs every plan the table holds.
 
 csrc/block_m_tuned.h: the M tile of the grouped GEMMs by mean token-expert pairs per
@@ -55,12 +56,15 @@ def dense_rows(records):
         prev = 0
         for r in rs:
             M = r["M"]
+            # plans whose split-K partials fit the static scratch (16-column tiles need none)
             ok = [p for p in r["plans"]
-                  if kb_per_split(K, p[2])[1] == 1 or kb_per_split(K, p[2])[1] * M * N * 4 + 256 <= STATIC_SCRATCH_BYTES]
+                  if p[1] == 16 or kb_per_split(K, p[2])[1] == 1
+                  or kb_per_split(K, p[2])[1] * M * N * 4 + 256 <= STATIC_SCRATCH_BYTES]
             if ok:
                 bm, bnb, sp, us = min(ok, key=lambda p: p[3])
-                if us < (1.0 - MARGIN) * r["default_us"]:
-                    rows.append((prev + 1, M, N, K, bm, bnb, sp, us, r["default_us"]))
+                base = r["rule"][3] if "rule" in r else r["default_us"]  # the rule's plan, timed
+                if us < (1.0 - MARGIN) * base:
+                    rows.append((prev + 1, M, N, K, bm, bnb, sp, us, base))
             prev = M
     return rows
 

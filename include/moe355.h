@@ -263,9 +263,12 @@ int gemm_fp8_blockscale(const uint8_t* a8, const float* a_scale,
  * columns (128 or 256), and K split into `splits` runs of whole 128-wide blocks whose
  * fp32 partial sums are added in a fixed order.  splits > 1 needs a workspace of
  * gemm_fp8_blockscale_tiled_workspace() bytes (MOE355_EINVAL without it); a run of more
- * than 128 K blocks is MOE355_EUNSUPPORTED.  Arguments, results and other errors are
- * those of gemm_fp8_blockscale (the arithmetic per output element is the same, whatever
- * the tiling; only the order of the split sums can differ).
+ * than 128 K blocks is MOE355_EUNSUPPORTED.  tile_n 16 selects the small-M kernel: one
+ * workgroup per 16 columns whose waves split K among themselves and add their fp32
+ * partial tiles in LDS in a fixed order (M <= tile_m <= 64, splits 1, no workspace,
+ * any K).  Arguments, results and other errors are those of gemm_fp8_blockscale (the
+ * arithmetic per output element is the same block-scaled sum whatever the tiling; only
+ * the order of the fp32 additions differs between K splits).
  */
 int gemm_fp8_blockscale_tiled(const uint8_t* a8, const float* a_scale,
                               int64_t sstride_m, int64_t sstride_kb,
@@ -275,6 +278,12 @@ int gemm_fp8_blockscale_tiled(const uint8_t* a8, const float* a_scale,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 /* Host-only: the workspace gemm_fp8_blockscale_tiled needs for this shape and split count. */
 int gemm_fp8_blockscale_tiled_workspace(int M, int N, int K, int splits, size_t* bytes);
+
+/* Host-only: the tiling gemm_fp8_blockscale runs for this shape (with its workspace):
+ * measured 1 -> the plan the call uses (the compiled table of measured plans, else the
+ * rule); measured 0 -> the rule alone (what a sweep compares the candidates against).
+ * Arguments and errors as gemm_fp8_blockscale_workspace. */
+int gemm_fp8_blockscale_plan(int M, int N, int K, int measured, int* tile_m, int* tile_n, int* splits);
 
 /*
  * gemm_fp8_blockscale for callers that cannot allocate device memory (code under

@@ -29,7 +29,12 @@ int main(void) {
   size_t bytes = 1;
   EXPECT(moe_down_combine_workspace(64, 7168, 8, &bytes) == MOE355_OK && bytes >= (size_t)64 * 8 * 7168 * 4);
   EXPECT(gemm_fp8_blockscale_workspace(4096, 18432, 7168, &bytes) == MOE355_OK && bytes == 0);
-  EXPECT(gemm_fp8_blockscale_workspace(1, 2048, 7168, &bytes) == MOE355_OK && bytes > 0);
+  /* the workspace follows the plan the call runs; the rule alone splits K at M = 64 */
+  int tm = 0, tn = 0, sp = 0;
+  EXPECT(gemm_fp8_blockscale_plan(64, 2048, 7168, 0, &tm, &tn, &sp) == MOE355_OK && sp > 1);
+  EXPECT(gemm_fp8_blockscale_plan(1, 2048, 7168, 1, &tm, &tn, &sp) == MOE355_OK);
+  EXPECT(gemm_fp8_blockscale_workspace(1, 2048, 7168, &bytes) == MOE355_OK &&
+         bytes == (sp > 1 ? (size_t)sp * 2048 * 4 + 256 : 0));
 
   /* every status has a text */
   const int codes[] = {MOE355_OK, MOE355_EINVAL, MOE355_EUNSUPPORTED, MOE355_EMISALIGNED, MOE355_ELAUNCH};

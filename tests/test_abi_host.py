@@ -122,10 +122,14 @@ def test_invalid_arguments_return_codes(lib):
 
 def test_dense_workspace_query(lib):
     from fp8_block_scaled_grouped_amd import moe355
-    # small M splits K (needs fp32 partials), large M does not
+    # the rule: small M splits K (needs fp32 partials), large M does not; the workspace
+    # follows the plan the call runs (the measured table's where it has an entry)
     for M, N in [(1, 2048), (1, 18432), (64, 2048), (16, 7168)]:
+        tm, tn, sp = moe355.gemm_fp8_blockscale_plan(M, N, 7168, measured=False)
+        assert sp >= 2 and tn in (128, 256) and tm == (16 if M <= 16 else 64), (M, N, tm, tn, sp)
+        tm, tn, sp = moe355.gemm_fp8_blockscale_plan(M, N, 7168)
         n = moe355.gemm_fp8_blockscale_workspace(M, N, 7168)
-        assert n >= 2 * M * N * 4, (M, N, n)
+        assert n == (sp * M * N * 4 + 256 if sp > 1 else 0), (M, N, n, sp)
         assert n <= M * N * 4 * 56 + 256
     assert moe355.gemm_fp8_blockscale_workspace(4096, 18432, 7168) == 0
     assert moe355.gemm_fp8_blockscale_workspace(0, 2048, 7168) == 0

@@ -569,4 +569,31 @@ def test_dense_tiled_rejects(m):
     with pytest.raises(RuntimeError):  # a split without workspace
         m.gemm_fp8_blockscale_tiled(a8, sa, d["b"], d["b_scale"], 16, 128, 2,
                                     workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    with pytest.raises(RuntimeError):  # 16-column tiles split K inside the workgroup only
+        m.gemm_fp8_blockscale_tiled(a8, sa, d["b"], d["b_scale"], 16, 16, 2)
+    with pytest.raises(RuntimeError):  # ... and take at most tile_m (<= 64) rows
+        m.gemm_fp8_blockscale_tiled(a8[:8], sa[:8], d["b"], d["b_scale"], 128, 16, 1)
     torch.cuda.synchronize()
+
+
+# the small-M kernel (16-column tiles, K split over the waves of a workgroup and summed
+# in LDS in wave order): against the oracle, deterministic, on ragged M (1, 2 and 4
+# tiles of 16 rows), N off a multiple of 16, partial and short K, K above 16,384
+@pytest.mark.parametrize("M,N,K", [(1, 2048, 7168), (5, 576, 1040), (8, 1000, 4112), (37, 136, 64),
+                                   (64, 4104, 7184), (17, 256, 18432), (50, 384, 512)])
+@pytest.mark.parametrize("layout", ["row", "kblock"])
+def test_dense_small_m_kernel(m, M, N, K, layout):
+    from fp8_block_scaled_grouped_amd import inputs
+    print("dense small-M", M, N, K, layout, flush=True)
+    d = inputs.make_dense_inputs(M, N, K, "cpu", seed=M + 5 * N + K)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(d["a"]))
+    sa_dev = torch.from_numpy(sa if layout == "row" else np.ascontiguousarray(sa.T)).to(DEV)
+    args = (torch.from_numpy(a8).to(DEV), sa_dev, d["b"].to(DEV), d["b_scale"].to(DEV))
+    tm = 16 * -(-M // 16)
+    tm = 64 if tm > 32 else tm
+    c1 = m.gemm_fp8_blockscale_tiled(*args, tm, 16, 1, scale_layout=layout).clone()
+    c2 = m.gemm_fp8_blockscale_tiled(*args, tm, 16, 1, scale_layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+    ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
+    assert_rel_max(f32_of_bf16(c1), ref, what="dense small-M %dx%dx%d" % (M, N, K))

@@ -9,8 +9,9 @@ from fp8_block_scaled_grouped_amd.tuning import make_tables as mt
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _rec(M, N, K, default_us, plans):
-    return {"sweep": "dense", "layer": "x", "M": M, "N": N, "K": K, "default_us": default_us, "plans": plans}
+def _rec(M, N, K, rule_us, plans):
+    return {"sweep": "dense", "layer": "x", "M": M, "N": N, "K": K, "default_us": 1e9,
+            "rule": [16, 128, 1, rule_us], "plans": plans}
 
 
 def test_dense_rows_margin_ranges_and_scratch_cap():
@@ -74,7 +75,7 @@ def test_library_plans_follow_the_dense_table():
     rows = mt.dense_rows(mt.read(path, "dense"))
     assert rows
     for m0, m1, n, k, bm, bnb, sp, us, dus in rows:
-        runs = mt.kb_per_split(k, sp)[1]
+        runs = 1 if bnb == 16 else mt.kb_per_split(k, sp)[1]
         for M in (m0, m1):
             want = runs * M * n * 4 + 256 if runs > 1 else 0
             assert moe355.gemm_fp8_blockscale_workspace(M, n, k) == want, (M, n, k, sp)
