@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None, help="token count of a MoE workload (default: its own)")
     ap.add_argument("--no-decode", action="store_true", help="prefill: leave out the decode layer beside it")
     ap.add_argument("--sweep", choices=["block_m", "dense"], default=None)
+    ap.add_argument("--phases", action="store_true",
+                    help="per-step phase clocks of the gate/up kernel from the diagnostic library libmoe355_trace.so")
     ap.add_argument("--graph", action="store_true",
                     help="also time the layer captured once as a HIP graph and replayed (graph_ms_per_step)")
     ap.add_argument("--fused", action="store_true",
@@ -583,6 +585,53 @@ def sweep_dense(a):
         torch.cuda.empty_cache()
 
 
+def phases(a):
+    """Per-step phase clocks of the gate/up kernel (128-row tiles) from the diagnostic
+    library libmoe355_trace.so: for K steps 1 .. KB-2 of every traced tile and wave, the
+    shader cycles spent waiting for the wave's own stage DMAs, at the barrier that
+    publishes the stage, and computing (MFMAs, folds, fragment reads, the next stage's
+    DMA issues) until the next step starts."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from fp8_block_scaled_grouped_amd import moe355
+    path = os.path.join(ROOT, "fp8_block_scaled_grouped_amd", "libmoe355_trace.so")
+    if not os.path.exists(path):
+        sys.exit("bench.py --phases: %s is not built (python -m fp8_block_scaled_grouped_amd.build)" % path)
+    moe355.LIB_PATH, moe355._lib = path, None
+    import fp8_block_scaled_grouped_amd as m
+
+    wl = a.workload if a.workload in ("prefill", "skew", "prefill_bias0", "skew_zipf") else "prefill"
+    cfg = moe_config(wl, a.tokens)
+    x = moe_inputs(cfg, a.seed)
+    layer = m.MoELayer(cfg, x["bias"], x["w1"], x["w1_scale"], x["w2"], x["w2_scale"], block_m=128)
+    for _ in range(max(a.warmup, 1) + 1):  # the trace keeps the last launch's tiles [0, 64)
+        layer.forward(x["hidden"], x["logits"])
+    torch.cuda.synchronize()
+    n = 64 * 8 * 64 * 3
+    buf = np.zeros(n, np.uint32)
+    fn = m.lib().moe355_phase_trace_read
+    fn.argtypes, fn.restype = [ctypes.c_void_p, ctypes.c_size_t], ctypes.c_int
+    if fn(buf.ctypes.data, n) != 0:
+        sys.exit("bench.py --phases: reading the trace failed")
+    t = buf.reshape(64, 8, 64, 3).astype(np.int64)
+    KB = min(cfg.H // 128, 64)
+    d = lambda x: (x % (1 << 32))  # clocks are the low 32 bits
+    wait = d(t[:, :, 1:KB - 1, 1] - t[:, :, 1:KB - 1, 0])
+    barrier = d(t[:, :, 1:KB - 1, 2] - t[:, :, 1:KB - 1, 1])
+    compute = d(t[:, :, 2:KB, 0] - t[:, :, 1:KB - 1, 2])
+    step = d(t[:, :, 2:KB, 0] - t[:, :, 1:KB - 1, 0])
+    q = lambda v: {"median": float(np.median(v)), "mean": float(v.mean()), "p10": float(np.percentile(v, 10)),
+                   "p90": float(np.percentile(v, 90))}
+    print(json.dumps({"phases": "moe_fp8_blockscale_g1u1 (128-row tiles, 8 waves, 3 stages)", "workload": wl,
+                      "tokens": cfg.T, "k_steps": KB, "tiles_traced": 64, "unit": "shader clock cycles (s_memtime)",
+                      "per_step": {"stage_wait": q(wait), "barrier": q(barrier), "compute": q(compute),
+                                   "step": q(step)},
+                      "stage_bytes": 48 * 1024, "mfma_cycles_per_step_per_simd": 1024}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -594,6 +643,9 @@ def main():
         return
     if a.sweep == "dense":
         sweep_dense(a)
+        return
+    if a.phases:
+        phases(a)
         return
     res = bench_dense(a) if a.workload == "dense" else bench_moe(a)
     if a.copy_calibration:

@@ -15,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe355.so")
+TRACE_LIB = os.path.join(PKG, "libmoe355_trace.so")
 SOURCES = ["gemm.hip", "gemm_big.hip", "dense_small.hip", "topk.hip", "sort.hip", "quant.hip", "shuffle.hip", "status.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -30,11 +31,11 @@ HIP_FLAGS = [
 ]
 
 
-def _compile(src, save_temps, verbose):
+def _compile(src, save_temps, verbose, trace=False):
     path = os.path.join(CSRC, src)
-    obj = os.path.join(CSRC, "_obj", src + ".o")
+    obj = os.path.join(CSRC, "_obj", src + (".trace.o" if trace else ".o"))
     os.makedirs(os.path.dirname(obj), exist_ok=True)
-    cmd = [HIPCC] + HIP_FLAGS + EXTRA.get(src, []) + ["-c", path, "-o", obj]
+    cmd = [HIPCC] + HIP_FLAGS + EXTRA.get(src, []) + (["-DMOE355_PHASE_TRACE"] if trace else []) + ["-c", path, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"), "-c", path, "-o", obj]
     if save_temps and src.endswith(".hip"):
@@ -51,17 +52,31 @@ def _compile(src, save_temps, verbose):
     return obj
 
 
-def build(save_temps=None, verbose=False):
-    # the sources compile independently (gemm.hip, the longest, first)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(lambda src: _compile(src, save_temps, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _trace_obj(obj, trace_obj):
+    """The object of the diagnostic library: the traced gemm.hip in place of the plain one."""
+    return trace_obj if obj.endswith(os.sep + "gemm.hip.o") else obj
+
+
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("link of libmoe355.so failed")
-    os.replace(tmp, LIB)
+        raise RuntimeError("link of %s failed" % os.path.basename(lib))
+    os.replace(tmp, lib)
+
+
+def build(save_temps=None, verbose=False, trace=True):
+    """Builds libmoe355.so and (trace) libmoe355_trace.so, the diagnostic variant whose
+    gate/up kernel records per-step phase clocks (bench.py --phases)."""
+    # the sources compile independently (gemm.hip, the longest, first)
+    jobs = [(src, False) for src in SOURCES] + ([("gemm.hip", True)] if trace else [])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=5) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], save_temps, verbose, j[1]), jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    if trace:
+        _link([_trace_obj(o, objs[-1]) for o in objs[:len(SOURCES)]], TRACE_LIB)
     return LIB
 
 

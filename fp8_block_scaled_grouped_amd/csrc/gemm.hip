@@ -103,7 +103,23 @@ struct GemmSmem {
   __attribute__((aligned(16))) uint8_t lds[C::kLds];
   int rowinfo[C::BM];
   float red[C::kRed][C::kEpR];
+#ifdef MOE355_PHASE_TRACE
+  uint32_t trace[8][64][3];  // per wave and K step: clock before the wait, after it, after the barrier
+#endif
 };
+
+#ifdef MOE355_PHASE_TRACE
+}  // namespace
+}  // namespace moe355
+#include "../../include/moe355_trace.h"
+namespace moe355 {
+namespace {
+// Diagnostic build only (libmoe355_trace.so): per-step phase clocks (s_memtime) of the
+// gate/up kernel on 128-row tiles, tiles [0, kTraceTiles) of each launch, up to 64 K
+// steps, read back with moe355_phase_trace_read.
+constexpr int kTraceTiles = 64;
+__device__ uint32_t g_phase_trace[kTraceTiles][8][64][3];
+#endif
 
 // One output tile (tile index `tile_id` of the launch grid) with the workgroup's LDS.
 // Every thread of the workgroup calls it with the same tile; it returns (uniformly)
@@ -317,12 +333,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
   auto step = [&](const int kb, const int stage, auto tmv_c, auto rf_c) {
     constexpr int TMV = decltype(tmv_c)::value;
     constexpr int RF = decltype(rf_c)::value;
+#ifdef MOE355_PHASE_TRACE
+    constexpr bool kTrace = MODE == kG1U1 && C::BM == 128;
+    uint32_t* const tr = kTrace ? &sm.trace[w][min(kb, 63)][0] : nullptr;
+    if constexpr (kTrace) tr[0] = (uint32_t)__builtin_amdgcn_s_memtime();
+#endif
     if constexpr (RF == 1) {
       vm_wait<(C::S - 2) * C::kLoadsPerStage>();
     } else {
       vm_wait_stages<C::kLoadsPerStage>(min(C::S - 2, KBp - 1 - kb));
     }
+#ifdef MOE355_PHASE_TRACE
+    if constexpr (kTrace) tr[1] = (uint32_t)__builtin_amdgcn_s_memtime();
+#endif
     barrier_only();
+#ifdef MOE355_PHASE_TRACE
+    if constexpr (kTrace) tr[2] = (uint32_t)__builtin_amdgcn_s_memtime();
+#endif
     const bool refill = RF == 1 || kb + C::S - 1 < KBp;
     const int nstage = (stage + C::S - 1) % C::S, nkb = kb + C::S - 1;
     if constexpr (TMV == 0) {
@@ -423,6 +450,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
   }
   vm_wait<0>();
   __syncthreads();
+#ifdef MOE355_PHASE_TRACE
+  if constexpr (MODE == kG1U1 && C::BM == 128) {
+    if (tile_id < kTraceTiles)
+#pragma unroll
+      for (int i = 0; i < 3; ++i) g_phase_trace[tile_id][w][lane][i] = sm.trace[w][lane][i];
+  }
+#endif
 
   // ---- epilogues (LDS is free again)
   if (MODE == kDense && C::BM <= 128 && g.splits > 1) {
@@ -1256,3 +1290,13 @@ extern "C" int moe_fp8_blockscale_fused(const uint8_t* a8, const float* a_scale,
   f.ld_out = ld_out;
   return launch_fused(f, block_m, stream);
 }
+
+#ifdef MOE355_PHASE_TRACE
+extern "C" int moe355_phase_trace_read(uint32_t* host, size_t count) {
+  MOE355_CHECK(host && count <= sizeof(g_phase_trace) / sizeof(uint32_t), MOE355_EINVAL);
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_trace), count * sizeof(uint32_t), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess
+             ? MOE355_OK
+             : MOE355_ELAUNCH;
+}
+#endif

@@ -195,3 +195,16 @@ def test_binding_checks_run_on_the_host():
         moe355._need(torch.zeros(4), (4,), torch.float32, "x")       # not a GPU tensor
     with pytest.raises(ValueError):
         moe355._scale_strides(torch.zeros((2, 2)), 2, 256, "columns")
+
+
+def test_trace_library_exports():
+    # the diagnostic build carries the whole ABI plus the phase-trace readback
+    path = os.path.join(ROOT, "fp8_block_scaled_grouped_amd", "libmoe355_trace.so")
+    if not os.path.exists(path):
+        pytest.skip("libmoe355_trace.so not built")
+    lib = ctypes.CDLL(path)
+    for name in _declared() + ["moe355_phase_trace_read"]:
+        assert hasattr(lib, name), name
+    fn = lib.moe355_phase_trace_read
+    fn.argtypes, fn.restype = [ctypes.c_void_p, ctypes.c_size_t], ctypes.c_int
+    assert fn(None, 1) == -1  # host-side check, no GPU touched
