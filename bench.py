@@ -625,10 +625,13 @@ def phases(a):
     step = d(t[:, :, 2:KB, 0] - t[:, :, 1:KB - 1, 0])
     q = lambda v: {"median": float(np.median(v)), "mean": float(v.mean()), "p10": float(np.percentile(v, 10)),
                    "p90": float(np.percentile(v, 90))}
+    per_wave = {ph: [float(np.median(v[:, w_])) for w_ in range(8)]
+                for ph, v in (("stage_wait", wait), ("barrier", barrier), ("compute", compute))}
     print(json.dumps({"phases": "moe_fp8_blockscale_g1u1 (128-row tiles, 8 waves, 3 stages)", "workload": wl,
                       "tokens": cfg.T, "k_steps": KB, "tiles_traced": 64, "unit": "shader clock cycles (s_memtime)",
                       "per_step": {"stage_wait": q(wait), "barrier": q(barrier), "compute": q(compute),
                                    "step": q(step)},
+                      "per_wave_median": per_wave,
                       "stage_bytes": 48 * 1024, "mfma_cycles_per_step_per_simd": 1024}), flush=True)
 
 
