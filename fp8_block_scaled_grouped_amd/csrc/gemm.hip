@@ -49,6 +49,7 @@ namespace {
 template <int MODE, int BM_, int BNB_, int NW_, int WM_, int S_>
 struct Cfg {
   static constexpr int BM = BM_, BNB = BNB_, NW = NW_, WM = WM_, S = S_;
+  static constexpr int kMode = MODE;
   static constexpr int kThreads = NW * 64;
   static constexpr int kWN = NW / WM;
   static constexpr int kParts = MODE == kG1U1 ? 2 : 1;
@@ -84,7 +85,7 @@ struct Cfg {
   static_assert(MODE != kG1U1 || BNB == 256, "g1u1 stages 128 gate and 128 up rows");
   static_assert(kWN % kParts == 0, "gate and up waves split evenly");
   static_assert(S >= 2 && S <= 4 && 2 * kLoadsPerStage < 64, "pipeline depth");
-  static_assert(kLds + BM * 4 + kRed * kEpR * 4 <= 160 * 1024, "LDS of one workgroup");
+  static_assert(kLds + (MODE == kDown ? 2 : 1) * BM * 4 + kRed * kEpR * 4 <= 160 * 1024, "LDS of one workgroup");
 };
 
 
@@ -102,6 +103,7 @@ template <class C>
 struct GemmSmem {
   __attribute__((aligned(16))) uint8_t lds[C::kLds];
   int rowinfo[C::BM];
+  float roww[C::kMode == kDown ? C::BM : 1];  // down: routing weights of the tile's rows
   float red[C::kRed][C::kEpR];
 #ifdef MOE355_PHASE_TRACE
   uint32_t trace[8][64][3];  // per wave and K step: clock before the wait, after it, after the barrier
@@ -201,7 +203,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
   const float sbv1 = lane + 64 < KB ? sbp[lane + 64] : 0.0f;
 
   if constexpr (MODE != kDense) {
-    for (int i = tid; i < C::BM; i += C::kThreads) rowinfo[i] = g.sorted_ids[row0 + i];
+    for (int i = tid; i < C::BM; i += C::kThreads) {
+      rowinfo[i] = g.sorted_ids[row0 + i];
+      // down: the weights too, so that the epilogue reads them from LDS
+      if constexpr (MODE == kDown) sm.roww[i] = g.sorted_w[row0 + i];
+    }
     __syncthreads();
     nrows = __syncthreads_count(tid < C::BM && rowinfo[tid < C::BM ? tid : 0] < npairs);
   } else {
@@ -516,7 +522,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
         const int rl = wm * C::kWTM + tm * 16 + 4 * lg + i;
         const int pid = rowinfo[rl];
         if (row0 + rl < nvalid && pid < npairs) {
-          const float wgt = g.sorted_w[row0 + rl];
+          const float wgt = sm.roww[rl];
           float* yr = g.y + (int64_t)pid * g.N + (int64_t)nt * C::BNB + wn * C::kWTNB + lr;
 #pragma unroll
           for (int tn = 0; tn < C::kTN; ++tn) yr[tn * 16] = acc[tm][tn][i] * wgt;
