@@ -44,6 +44,10 @@ def role(name):
     if m:
         mode, bm, bnb, nw, _, st = (int(x) for x in m.groups())
         return MODES[mode], "%s (BM %d, B rows %d, %d waves, %d stages)" % (MODES[mode], bm, bnb, nw, st)
+    m = re.search(r"dense_small_kernel<(\d+), (true|false)>", name)
+    if m:
+        return "dense", "dense small-M (%d row tiles, 8 waves, %s B)" % (
+            int(m.group(1)), "pre-shuffled" if m.group(2) == "true" else "plain")
     m = re.search(r"big_gemm_kernel<(\d+)", name)
     if m:
         mode = int(m.group(1))

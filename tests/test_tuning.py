@@ -86,6 +86,8 @@ def test_rocprof_summary_roles_and_traffic_scaling(tmp_path):
     g1u1 = "void moe355::(anonymous namespace)::bs_gemm_kernel<moe355::(anonymous namespace)::Cfg<1, 128, 256, 8, 2, 3>, 1, false, false>(moe355::GemmArgs)"
     assert rs.role(g1u1) == ("g1u1", "g1u1 (BM 128, B rows 256, 8 waves, 3 stages)")
     assert rs.role("big_gemm_kernel<2, false>")[0] == "down"
+    small = "void moe355::(anonymous namespace)::dense_small_kernel<1, false>(moe355::DenseSmallArgs)"
+    assert rs.role(small) == ("dense", "dense small-M (1 row tiles, 8 waves, plain B)")
     assert rs.role("__amd_rocclr_copyBuffer")[0] == "copy"
     assert rs.role("at::native::elementwise_kernel<...>")[0] is None
     # counters: two g1u1 dispatches and three calibration copies; bytes = KiB * copy bytes / copy KiB
