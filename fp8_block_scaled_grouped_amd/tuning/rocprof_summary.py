@@ -9,6 +9,10 @@
     mfma     --dir D --workload W --command C [--append] --out profiles/<name>.txt
              MFMA busy share, executed FP8 flops and clock per GEMM kernel from
              SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F8, SQ_BUSY_CU_CYCLES, GRBM_GUI_ACTIVE
+    mem      --dir D --workload W --command C [--append] --out profiles/<name>.txt
+             L2-miss reads per GEMM / combine kernel: count, mean latency and mean number in
+             flight (TCC_EA0_RDREQ, TCC_EA0_RDREQ_LEVEL) and the share of cycles the read
+             interface stalled for DRAM or GMI credits, against GRBM_GUI_ACTIVE
 
 Kernel roles come from the demangled names: bs_gemm_kernel<Cfg<mode, BM, B rows, waves, wave
 rows, stages>, ...> and big_gemm_kernel<mode, ...> with mode 0 dense, 1 gate/up, 2 down.
@@ -188,6 +192,55 @@ def cmd_mfma(a):
         f.write("\n".join(lines) + "\n\n")
 
 
+def mem_rows(d):
+    """Per kernel label: averages over its dispatches of the memory-side counters."""
+    per = {}
+    for f in find(d, "counter_collection.csv"):
+        for r in rows(f):
+            rl, label = role(r["Kernel_Name"])
+            if rl not in ("dense", "g1u1", "down", "combine", "fused_moe"):
+                continue
+            key = (label, r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            x = per.setdefault(key, {"dur": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+            x[r["Counter_Name"]] = x.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    by = {}
+    for (label, _), x in per.items():
+        by.setdefault(label, []).append(x)
+    out = {}
+    for label, xs in by.items():
+        n = len(xs)
+        avg = lambda k: sum(x.get(k, 0.0) for x in xs) / n
+        gui = avg("GRBM_GUI_ACTIVE") / 8  # cycles of one XCD (the counter sums the 8)
+        req, lvl = avg("TCC_EA0_RDREQ_sum"), avg("TCC_EA0_RDREQ_LEVEL_sum")
+        chan = gui * 128  # 16 L2 channels per XCD, 8 XCDs
+        out[label] = {"calls": n, "dur_us": avg("dur") / 1e3, "clock_ghz": gui / max(avg("dur"), 1.0),
+                      "reads": req, "latency_cycles": lvl / max(req, 1.0), "in_flight": lvl / max(gui, 1.0),
+                      "dram_stall": avg("TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum") / max(chan, 1.0),
+                      "gmi_stall": avg("TCC_EA0_RDREQ_GMI_CREDIT_STALL_sum") / max(chan, 1.0)}
+    return out
+
+
+def cmd_mem(a):
+    lines = []
+    if not a.append:
+        lines += ["rocprofv3 memory-side counters per libmoe355 kernel (L2 misses)", "",
+                  "reads = TCC_EA0_RDREQ_sum (requests from the L2s to memory, mostly 128 B); latency =",
+                  "TCC_EA0_RDREQ_LEVEL_sum / reads (cycles from request to data); in flight = LEVEL_sum /",
+                  "(GRBM_GUI_ACTIVE / 8), the mean number of such reads outstanding over the chip; DRAM / GMI",
+                  "stall = TCC_EA0_RDREQ_{DRAM,GMI}_CREDIT_STALL_sum / (128 L2 channels x GUI / 8), the share of",
+                  "cycles a channel's read interface waited for credits. Durations are under the profiler.", ""]
+    lines += ["workload %s; command (<repo> = the repository root, <out> = any output directory):" % a.workload,
+              "  " + a.command,
+              "  %-44s %6s %9s %9s %12s %9s %10s %7s %7s" % ("kernel", "calls", "dur us", "clock GHz", "reads",
+                                                              "latency", "in flight", "DRAM", "GMI")]
+    for label, r in sorted(mem_rows(a.dir).items()):
+        lines.append("  %-44s %6d %9.1f %9.2f %12.4g %9.0f %10.0f %6.2f%% %6.2f%%" % (
+            label, r["calls"], r["dur_us"], r["clock_ghz"], r["reads"], r["latency_cycles"], r["in_flight"],
+            100 * r["dram_stall"], 100 * r["gmi_stall"]))
+    with open(a.out, "a" if a.append else "w") as f:
+        f.write("\n".join(lines) + "\n\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -211,8 +264,14 @@ def main():
     m.add_argument("--command", required=True)
     m.add_argument("--append", action="store_true")
     m.add_argument("--out", required=True)
+    e = sub.add_parser("mem")
+    e.add_argument("--dir", required=True)
+    e.add_argument("--workload", required=True)
+    e.add_argument("--command", required=True)
+    e.add_argument("--append", action="store_true")
+    e.add_argument("--out", required=True)
     a = ap.parse_args()
-    {"kt": cmd_kt, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
+    {"kt": cmd_kt, "traffic": cmd_traffic, "mfma": cmd_mfma, "mem": cmd_mem}[a.cmd](a)
 
 
 if __name__ == "__main__":

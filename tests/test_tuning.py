@@ -107,3 +107,26 @@ def test_rocprof_summary_roles_and_traffic_scaling(tmp_path):
     assert k["fetch_bytes"] == 200.0 * (1 << 20) / 512.0
     assert k["write_bytes"] == 20.0 * (1 << 20) / 1024.0
     assert k["dispatches"] == 2
+
+
+def test_rocprof_summary_memory_counters(tmp_path):
+    """The memory-side summary: latency = LEVEL / reads, in flight = LEVEL / (GUI / 8), stall
+    shares over 128 L2 channels, averaged over a kernel's dispatches."""
+    from fp8_block_scaled_grouped_amd.tuning import rocprof_summary as rs
+    down = "void moe355::(anonymous namespace)::bs_gemm_kernel<moe355::(anonymous namespace)::Cfg<2, 128, 256, 8, 2, 3>, 2, false, false>(moe355::GemmArgs)"
+    d = tmp_path / "mem" / "host"
+    d.mkdir(parents=True)
+    vals = {"TCC_EA0_RDREQ_sum": 1000.0, "TCC_EA0_RDREQ_LEVEL_sum": 500000.0, "GRBM_GUI_ACTIVE": 8 * 2000.0,
+            "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum": 128 * 2000.0 * 0.25, "TCC_EA0_RDREQ_GMI_CREDIT_STALL_sum": 0.0}
+    lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp"]
+    for disp in (1, 2):
+        lines += ['%d,"%s",%s,%f,0,1000' % (disp, down, k, v) for k, v in vals.items()]
+    lines += ['3,"at::native::elementwise_kernel<...>",TCC_EA0_RDREQ_sum,5,0,10']
+    (d / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+    r = rs.mem_rows(str(tmp_path / "mem"))
+    assert list(r) == ["down (BM 128, B rows 256, 8 waves, 3 stages)"]
+    x = r["down (BM 128, B rows 256, 8 waves, 3 stages)"]
+    assert x["calls"] == 2 and x["reads"] == 1000.0
+    assert x["latency_cycles"] == 500.0 and x["in_flight"] == 250.0
+    assert abs(x["dram_stall"] - 0.25) < 1e-12 and x["gmi_stall"] == 0.0
+    assert abs(x["clock_ghz"] - 2.0) < 1e-12
