@@ -208,3 +208,15 @@ def test_trace_library_exports():
     fn = lib.moe355_phase_trace_read
     fn.argtypes, fn.restype = [ctypes.c_void_p, ctypes.c_size_t], ctypes.c_int
     assert fn(None, 1) == -1  # host-side check, no GPU touched
+
+
+def test_lds_probe_built_for_gfx950():
+    # the LDS operand-traffic probe is a standalone program built with the library; its
+    # device code must be gfx950 code objects (checked from the bundle's target names)
+    path = os.path.join(ROOT, "fp8_block_scaled_grouped_amd", "lds_fill_probe")
+    if not os.path.exists(path):
+        pytest.skip("lds_fill_probe not built")
+    assert os.access(path, os.X_OK)
+    with open(path, "rb") as f:
+        blob = f.read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
