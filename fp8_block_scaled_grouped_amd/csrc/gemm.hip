@@ -330,9 +330,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
     for (int tn = 0; tn < C::kTN; ++tn) acc[tm][tn] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int s = 0; s < C::S - 1; ++s)
-    if (s < KBp) issue(s, s);
 
   // one K step on LDS stage `stage`; only the first TMV row tiles of the wave are computed
   // RF 1: the step refills its stage (steady state, no branches); RF 0: checked
@@ -405,6 +402,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
     }
   };
   // unrolled by the stage count: every LDS address is base + immediate
+  // (its first S - 1 stages are issued before the row-tile dispatch below)
   auto kloop = [&](auto tmv_c) {
     int kb0 = 0;
     // rounds whose every step refills (kb + S - 1 < KBp for the round's last step)
@@ -442,17 +440,155 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
       }
     }
   };
+  // K loop with the fragments of block kb + 1 read during step kb (whole K blocks only).
+  // Every fragment register takes the next block's data right after its last use in the
+  // step's MFMA sequence (weight fragments early in the step, activation fragments and
+  // their scales towards its end), so a step starts on operands already in registers
+  // instead of all waves reading LDS at once behind the barrier.  Step kb: wait for this
+  // wave's DMAs of block kb + 1, wait for its own LDS reads (they read block kb's stage,
+  // which is refilled next), barrier (block kb + 1 is published and no wave reads block kb's
+  // stage any more), refill block kb's stage with block kb + S, then block kb's MFMAs with
+  // block kb + 1's reads between them.  All S stages are in flight ahead of the registers.
+  constexpr int L = C::kLoadsPerStage;
+  static_assert(C::S * L < 64, "vmcnt range of the prefetching K loop");
+  auto wait_blocks = [&](int a) {  // at most a blocks of this wave's DMAs still outstanding
+    if (a >= 3) {
+      vm_wait<3 * L>();
+    } else if (a == 2) {
+      vm_wait<2 * L>();
+    } else if (a == 1) {
+      vm_wait<L>();
+    } else {
+      vm_wait<0>();
+    }
+  };
+  auto kloop_pf = [&](auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
+    constexpr int NQ = TMV * C::kTN;
+    static_assert(!C::kStreamA, "row tile fastest");
+#pragma unroll
+    for (int s = 0; s < C::S; ++s)
+      if (s < KBp) issue(s, s);
+    v8i av[TMV > 0 ? TMV : 1], bv[C::kTN];
+    v4f s4[TMV > 0 ? TMV : 1];
+    auto sb_of = [&](int kb) {
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? sbv0 : sbv1), kb & 63));
+    };
+    auto read_a = [&](const uint8_t* st, int tm) { av[tm] = lds_frag(st + C::kAOff, wm * C::kWTM + tm * 16, lane); };
+    auto read_s = [&](const uint8_t* st, int tm, float sb) {
+      s4[tm] = *reinterpret_cast<const v4f*>(st + sofs + (tm * 16 + 4 * lg) * 4) * sb;
+    };
+    auto read_b = [&](const uint8_t* st, int tn) { bv[tn] = lds_frag(st + C::kBOff, wn * C::kWTNB + tn * 16, lane); };
+    wait_blocks(min(C::S - 1, KBp - 1));
+    barrier_only();
+    if constexpr (TMV > 0) {
+      const float sb = sb_of(0);
+#pragma unroll
+      for (int tm = 0; tm < TMV; ++tm) {
+        read_a(lds, tm);
+        read_s(lds, tm, sb);
+      }
+#pragma unroll
+      for (int tn = 0; tn < C::kTN; ++tn) read_b(lds, tn);
+    }
+    // RF 1: the step refills (kb + S < KBp, no branches); RF 0: checked.  NX: block kb + 1 exists
+    auto step = [&](const int kb, const int stage, auto rf_c, auto nx_c) {
+      constexpr int RF = decltype(rf_c)::value;
+      constexpr int NX = decltype(nx_c)::value;
+#ifdef MOE355_PHASE_TRACE
+      constexpr bool kTrace = MODE == kG1U1 && C::BM == 128;
+      uint32_t* tr = nullptr;
+      if constexpr (kTrace) tr = &sm.trace[w][min(kb, 63)][0];
+      if constexpr (kTrace) tr[0] = (uint32_t)__builtin_amdgcn_s_memtime();
+#endif
+      if constexpr (NX) {
+        if constexpr (RF == 1) {
+          vm_wait<(C::S - 2) * L>();
+        } else {
+          wait_blocks(min(C::S - 2, KBp - 2 - kb));
+        }
+      }
+      lgkm_wait0();
+#ifdef MOE355_PHASE_TRACE
+      if constexpr (kTrace) tr[1] = (uint32_t)__builtin_amdgcn_s_memtime();
+#endif
+      barrier_only();
+#ifdef MOE355_PHASE_TRACE
+      if constexpr (kTrace) tr[2] = (uint32_t)__builtin_amdgcn_s_memtime();
+#endif
+      const bool refill = RF == 1 || kb + C::S < KBp;
+      const int nkb = kb + C::S;
+      if constexpr (TMV == 0) {
+        if (refill) issue(stage, nkb);
+      } else {
+        const uint8_t* nst = lds + ((stage + 1) % C::S) * C::kStage;
+        const float sbn = NX ? sb_of(kb + 1) : 0.0f;
+        // tile q: row tile q % TMV, column tile q / TMV; the refill DMAs of block kb's stage
+        // are spread between the MFMAs; the fold of q - 2 follows MFMA q
+        constexpr int kGap = NQ / L > 0 ? NQ / L : 1;
+        v4f tq[3];
+#pragma unroll
+        for (int q = 0; q < NQ + 2; ++q) {
+          if (q < NQ) tq[q % 3] = mfma16x16x128_fp8(av[q % TMV], bv[q / TMV], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int j = 0; j < L; ++j)
+            if (refill && (j * kGap < NQ + 1 ? j * kGap : NQ + 1) == q) issue_one(stage, nkb, j);
+          if (q >= 2) {
+            const int pq = q - 2;
+            acc[pq % TMV][pq / TMV] += tq[pq % 3] * s4[pq % TMV];
+          }
+          if constexpr (NX) {
+            if (q < NQ && q % TMV == TMV - 1) read_b(nst, q / TMV);        // last use of bv[q / TMV]
+            if (q < NQ && q / TMV == C::kTN - 1) read_a(nst, q % TMV);     // last use of av[q % TMV]
+            if (q >= 2 && (q - 2) / TMV == C::kTN - 1) read_s(nst, (q - 2) % TMV, sbn);  // its last fold
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    using One = std::integral_constant<int, 1>;
+    using Zero = std::integral_constant<int, 0>;
+    int kb0 = 0;
+    // rounds whose every step refills (kb + S < KBp for the round's last step)
+    for (; kb0 + 2 * C::S - 1 < KBp; kb0 += C::S) {
+#pragma unroll
+      for (int u = 0; u < C::S; ++u) step(kb0 + u, u, One{}, One{});
+    }
+    for (; kb0 < KBp; ++kb0) {
+      if (kb0 + 1 < KBp) {
+        step(kb0, kb0 % C::S, Zero{}, One{});
+      } else {
+        step(kb0, kb0 % C::S, Zero{}, Zero{});
+      }
+    }
+  };
   static_assert(C::kTM <= 8, "row tiles per wave");
+  // the prefetching loop for whole K blocks on tiles of 64 rows or more; 16- and 32-row
+  // tiles (decode-sized grouped blocks, split-K dense runs of a few K blocks) keep kloop,
+  // whose shallower prologue measured no slower there, and so does the partial block of PK
+  constexpr bool kPrefetch = !PK && !C::kStreamA && C::BM >= 64;
+  if constexpr (!kPrefetch) {
+#pragma unroll
+    for (int s = 0; s < C::S - 1; ++s)
+      if (s < KBp) issue(s, s);
+  }
+  auto kloop_any = [&](auto tmv_c) {
+    if constexpr (kPrefetch) {
+      kloop_pf(tmv_c);
+    } else {
+      kloop(tmv_c);
+    }
+  };
   switch (tm_live) {
-    case 0: kloop(std::integral_constant<int, 0>{}); break;
-    case 1: kloop(std::integral_constant<int, 1>{}); break;
-    case 2: if constexpr (C::kTM >= 2) kloop(std::integral_constant<int, 2>{}); break;
-    case 3: if constexpr (C::kTM >= 3) kloop(std::integral_constant<int, 3>{}); break;
-    case 4: if constexpr (C::kTM >= 4) kloop(std::integral_constant<int, 4>{}); break;
-    case 5: if constexpr (C::kTM >= 5) kloop(std::integral_constant<int, 5>{}); break;
-    case 6: if constexpr (C::kTM >= 6) kloop(std::integral_constant<int, 6>{}); break;
-    case 7: if constexpr (C::kTM >= 7) kloop(std::integral_constant<int, 7>{}); break;
-    default: if constexpr (C::kTM >= 8) kloop(std::integral_constant<int, 8>{}); break;
+    case 0: kloop_any(std::integral_constant<int, 0>{}); break;
+    case 1: kloop_any(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (C::kTM >= 2) kloop_any(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (C::kTM >= 3) kloop_any(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr (C::kTM >= 4) kloop_any(std::integral_constant<int, 4>{}); break;
+    case 5: if constexpr (C::kTM >= 5) kloop_any(std::integral_constant<int, 5>{}); break;
+    case 6: if constexpr (C::kTM >= 6) kloop_any(std::integral_constant<int, 6>{}); break;
+    case 7: if constexpr (C::kTM >= 7) kloop_any(std::integral_constant<int, 7>{}); break;
+    default: if constexpr (C::kTM >= 8) kloop_any(std::integral_constant<int, 8>{}); break;
   }
   vm_wait<0>();
   __syncthreads();
