@@ -273,6 +273,7 @@ __global__ __launch_bounds__(kThr) void big_gemm_kernel(GemmArgs g) {
   // row 64 wa + 16 t + lr.
   if constexpr (MODE == kDown) {
     // routing-weighted fp32 rows per flat pair: each lane stores 4 consecutive columns
+    // (non-temporal: the combine reads them once)
 #pragma unroll
     for (int t = 0; t < kAT; ++t) {
       const int r = 64 * wa + 16 * t + lr;
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(kThr) void big_gemm_kernel(GemmArgs g) {
         const float wgt = rowval[r];
         float* yr = g.y + (int64_t)pid * g.N + nt * kBW + 128 * wb + 4 * lg;
 #pragma unroll
-        for (int wt = 0; wt < kWT; ++wt) *reinterpret_cast<v4f*>(yr + 16 * wt) = acc[wt][t] * wgt;
+        for (int wt = 0; wt < kWT; ++wt) __builtin_nontemporal_store(acc[wt][t] * wgt, reinterpret_cast<v4f*>(yr + 16 * wt));
       }
     }
   } else {
