@@ -221,10 +221,8 @@ def time_layer(cfg, x, bm, steps, warmup, preshuffle=False, graph=False, per_cal
     start.record(stream)
     for i in range(steps):
         st[i].record(stream)
-        m.grouped_topk(logits, layer.bias, c.n_group, c.topk_group, c.topk, c.renorm, c.routed_scaling_factor,
-                       layer.topk_w, layer.topk_ids)
-        sid, sw, seid, nv = m.moe_sort(layer.topk_ids, layer.topk_w, c.E, bm, layer.sort_out, layer.sort_ws)
-        m.fp8_quant_1x128(hidden, layer.a8, layer.a_scale)
+        # routing, sort and (on the layer's side stream) quantisation, as MoELayer.forward runs them
+        sid, sw, seid, nv = layer.route_and_quantise(hidden, logits)
         ev[i][0].record(stream)
         if fused:
             m.moe_fp8_blockscale_fused(layer.a8, layer.a_scale, layer.w1, layer.w1_scale, layer.w2, layer.w2_scale,
@@ -339,7 +337,8 @@ def moe_report(cfg, bm, tm, workload, seed, preshuffle, fused=False):
                                "topk_group %d, top-%d, block_m %d" % (workload, T, H, I, cfg.E, cfg.n_group,
                                                                       cfg.topk_group, k, bm),
                    "tokens": T, "hidden": H, "intermediate": I, "experts": cfg.E, "topk": k, "block_m": bm,
-                   "preshuffled_weights": bool(preshuffle), "fused_expert_launch": bool(fused), "seed": seed},
+                   "preshuffled_weights": bool(preshuffle), "fused_expert_launch": bool(fused),
+                   "quantisation_on_side_stream": tm["layer"].side is not None, "seed": seed},
         "layer_tflops": flops / (ms * 1e-3) / 1e12, "layer_gbs": nbytes / (ms * 1e-3) / 1e9,
         "layer_frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,

@@ -446,11 +446,17 @@ class MoELayer:
 
     forward(hidden bf16 [T, H], logits fp32 [T, E]) -> bf16 [T, H], running
     grouped_topk -> moe_sort -> fp8_quant_1x128 -> moe_fp8_blockscale_g1u1 ->
-    moe_down_combine on the current stream.
+    moe_down_combine on the current stream.  With overlap_quant the quantisation, which
+    does not depend on the routing, runs on a second stream (default priority) beside
+    grouped_topk and moe_sort: it starts after everything already queued on the current
+    stream (so also after the previous forward's GEMMs, which read a8) and the GEMMs wait
+    for it.  Off by default: it measured within noise on the prefill layer (5.10 against
+    5.11 ms of serial calls) and 14 us slower on the 64-token decode layer, where the
+    cross-stream join costs more than the 6 us quantisation.
     """
 
     def __init__(self, cfg, bias, w1, w1_scale, w2, w2_scale, T=None, block_m=None, scale_layout="row",
-                 fc2_smooth_scale=None, preshuffle=False, fused=False):
+                 fc2_smooth_scale=None, preshuffle=False, fused=False, overlap_quant=False):
         self.cfg = cfg
         self.T = cfg.T if T is None else T
         if block_m is None:
@@ -478,6 +484,7 @@ class MoELayer:
         self.a_scale = torch.empty((T, H // 128) if scale_layout == "row" else (H // 128, T), dtype=torch.float32,
                                    device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.side = torch.cuda.Stream(device=dev) if overlap_quant else None
         # fused: the expert computation as one launch (moe_fp8_blockscale_fused), its
         # intermediates in one workspace; else the two calls on h8 / h_scale / down_ws
         self.fused = fused
@@ -491,12 +498,27 @@ class MoELayer:
             self.h_scale = torch.empty((ms, I // 128), dtype=torch.float32, device=dev)
             self.down_ws = torch.empty(moe_down_combine_workspace(T, H, k), dtype=torch.uint8, device=dev)
 
-    def forward(self, hidden, logits):
+    def route_and_quantise(self, hidden, logits):
+        """grouped_topk, moe_sort and fp8_quant_1x128 (on the side stream with overlap_quant);
+        returns the sort outputs.  On return the current stream is ordered after all three."""
         c = self.cfg
+        main = torch.cuda.current_stream()
+        if self.side is not None:
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                fp8_quant_1x128(hidden, self.a8, self.a_scale, self.scale_layout)
         grouped_topk(logits, self.bias, c.n_group, c.topk_group, c.topk, c.renorm, c.routed_scaling_factor,
                      self.topk_w, self.topk_ids)
-        sid, sw, seid, nv = moe_sort(self.topk_ids, self.topk_w, c.E, self.block_m, self.sort_out, self.sort_ws)
-        fp8_quant_1x128(hidden, self.a8, self.a_scale, self.scale_layout)
+        srt = moe_sort(self.topk_ids, self.topk_w, c.E, self.block_m, self.sort_out, self.sort_ws)
+        if self.side is not None:
+            main.wait_stream(self.side)
+        else:
+            fp8_quant_1x128(hidden, self.a8, self.a_scale, self.scale_layout)
+        return srt
+
+    def forward(self, hidden, logits):
+        c = self.cfg
+        sid, sw, seid, nv = self.route_and_quantise(hidden, logits)
         if self.fused:
             return moe_fp8_blockscale_fused(self.a8, self.a_scale, self.w1, self.w1_scale, self.w2, self.w2_scale, sid,
                                             sw, seid, nv, c.topk, self.block_m, self.out, self.fused_ws,

@@ -380,9 +380,11 @@ def test_layer_tiny_preshuffled_bitwise(m, tiny, BM):
 def test_layer_graph_replay_matches_eager(m, tiny, BM):
     # the five calls allocate nothing and never synchronise: captured once as a graph, every
     # replay (with eager work and synchronisations between replays) reproduces the eager output
+    # (with the quantisation on the layer's side stream: the capture forks and joins it)
     cfg, x = tiny
     g = {k: v.to(DEV) for k, v in x.items()}
-    layer = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"], block_m=BM)
+    layer = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"], block_m=BM,
+                       overlap_quant=True)
     eager = layer.forward(g["hidden"], g["logits"]).clone()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -396,6 +398,29 @@ def test_layer_graph_replay_matches_eager(m, tiny, BM):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(layer.out.view(torch.int16), eager.view(torch.int16)), "replay %d" % i
+
+
+@pytest.mark.parametrize("BM", [16, 128])
+def test_layer_quant_overlap_matches_serial(m, tiny, BM):
+    # quantisation on the layer's side stream gives the serial layer's output bit for bit,
+    # also over two back-to-back calls on different inputs (the second call's quantisation
+    # must wait for the first call's GEMMs, which read the same a8 buffer)
+    cfg, x = tiny
+    g = {k: v.to(DEV) for k, v in x.items()}
+    h2 = (g["hidden"].float() * -0.75).to(torch.bfloat16)
+    lg2 = g["logits"].flip(1).contiguous()
+    over = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"], block_m=BM,
+                      overlap_quant=True)
+    serial = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"], block_m=BM)
+    assert over.side is not None and serial.side is None
+    o1 = over.forward(g["hidden"], g["logits"]).clone()
+    o2 = over.forward(h2, lg2).clone()
+    s1 = serial.forward(g["hidden"], g["logits"]).clone()
+    s2 = serial.forward(h2, lg2).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), s1.view(torch.int16))
+    assert torch.equal(o2.view(torch.int16), s2.view(torch.int16))
+    assert not torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
 def test_binding_rejects_wrong_shapes(m, tiny):
