@@ -16,8 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe355.so")
 TRACE_LIB = os.path.join(PKG, "libmoe355_trace.so")
-PROBE_SRC = os.path.join(PKG, "tuning", "lds_fill_probe.hip")
-PROBE = os.path.join(PKG, "lds_fill_probe")
+# standalone probe programs (tuning/<name>.hip -> <package>/<name>)
+PROBES = ["lds_fill_probe", "kstep_probe"]
 SOURCES = ["gemm.hip", "gemm_big.hip", "dense_small.hip", "topk.hip", "sort.hip", "quant.hip", "shuffle.hip", "status.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -69,30 +69,34 @@ def _link(objs, lib):
     os.replace(tmp, lib)
 
 
-def _probe(verbose):
-    """The LDS operand-traffic probe (a standalone program, tuning/lds_fill_probe.hip)."""
-    tmp = PROBE + ".tmp"
-    cmd = [HIPCC] + HIP_FLAGS + [PROBE_SRC, "-o", tmp]
+def _probe(name, verbose):
+    """One standalone probe program: tuning/<name>.hip built to <package>/<name>."""
+    out = os.path.join(PKG, name)
+    tmp = out + ".tmp"
+    cmd = [HIPCC] + HIP_FLAGS + ["-mllvm", "-amdgpu-mfma-vgpr-form", os.path.join(PKG, "tuning", name + ".hip"),
+                                 "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed on lds_fill_probe.hip")
-    os.replace(tmp, PROBE)
-    return PROBE
+        raise RuntimeError("hipcc failed on %s.hip" % name)
+    os.replace(tmp, out)
+    return out
 
 
 def build(save_temps=None, verbose=False, trace=True):
     """Builds libmoe355.so, (trace) libmoe355_trace.so, the diagnostic variant whose
-    gate/up kernel records per-step phase clocks (bench.py --phases), and the LDS
-    operand-traffic probe program lds_fill_probe."""
+    gate/up kernel records per-step phase clocks (bench.py --phases), and the probe
+    programs lds_fill_probe (LDS fill and operand traffic) and kstep_probe (the engine's
+    K step alone)."""
     # the sources compile independently (gemm.hip, the longest, first)
     jobs = [(src, False) for src in SOURCES] + ([("gemm.hip", True)] if trace else [])
     with concurrent.futures.ThreadPoolExecutor(max_workers=5) as ex:
-        probe = ex.submit(_probe, verbose)
+        probes = [ex.submit(_probe, name, verbose) for name in PROBES]
         objs = list(ex.map(lambda j: _compile(j[0], save_temps, verbose, j[1]), jobs))
-        probe.result()
+        for pr in probes:
+            pr.result()
     _link(objs[:len(SOURCES)], LIB)
     if trace:
         _link([_trace_obj(o, objs[-1]) for o in objs[:len(SOURCES)]], TRACE_LIB)

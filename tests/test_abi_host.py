@@ -210,12 +210,13 @@ def test_trace_library_exports():
     assert fn(None, 1) == -1  # host-side check, no GPU touched
 
 
-def test_lds_probe_built_for_gfx950():
-    # the LDS operand-traffic probe is a standalone program built with the library; its
-    # device code must be gfx950 code objects (checked from the bundle's target names)
-    path = os.path.join(ROOT, "fp8_block_scaled_grouped_amd", "lds_fill_probe")
+@pytest.mark.parametrize("name", ["lds_fill_probe", "kstep_probe"])
+def test_probes_built_for_gfx950(name):
+    # the probe programs are built with the library; their device code must be gfx950 code
+    # objects (checked from the bundle's target names)
+    path = os.path.join(ROOT, "fp8_block_scaled_grouped_amd", name)
     if not os.path.exists(path):
-        pytest.skip("lds_fill_probe not built")
+        pytest.skip(name + " not built")
     assert os.access(path, os.X_OK)
     with open(path, "rb") as f:
         blob = f.read()
