@@ -583,6 +583,53 @@ def test_dense_tiled_plans(m, M, N, K):
     assert torch.equal(c.view(torch.int16), t.view(torch.int16)), sp
 
 
+# The 64- and 128-row tiles run the K loop that reads the next K block's fragments during the
+# current block's MFMAs; K from one block (fewer than its 3 stages) to 11 blocks covers the
+# unrolled rounds and tails of every length.  Every tiling gives the same bits (the block sums
+# are added in the same K order) and matches the oracle.
+@pytest.mark.parametrize("K", [128, 256, 384, 512, 640, 768, 896, 1152, 1408])
+def test_dense_k_steps_all_tilings(m, K):
+    from fp8_block_scaled_grouped_amd import inputs
+    M, N = 200, 384
+    print("dense K steps", M, N, K, flush=True)
+    d = inputs.make_dense_inputs(M, N, K, "cpu", seed=K)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(d["a"]))
+    ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
+    args = (torch.from_numpy(a8).to(DEV), torch.from_numpy(sa).to(DEV), d["b"].to(DEV), d["b_scale"].to(DEV))
+    outs = {}
+    for bm in (16, 64, 128):
+        for bn in (128, 256):
+            outs[(bm, bn)] = m.gemm_fp8_blockscale_tiled(*args, bm, bn, 1).view(torch.int16).cpu()
+    first = outs[(16, 128)]
+    for key, v in outs.items():
+        assert torch.equal(v, first), key
+    assert_rel_max(f32_of_bf16(first.view(torch.bfloat16)), ref, what="dense K %d" % K)
+
+
+# The grouped GEMMs over K sweeps: g1u1's K is H, down's K is I.  The layer output is the same
+# bits at block_m 16 (the plain K loop) and 64 / 128 (fragments one block ahead) and matches
+# the oracle.
+@pytest.mark.parametrize("H,I", [(512, 128), (768, 384), (1280, 640)])
+def test_layer_k_steps_all_block_m(m, H, I):
+    from fp8_block_scaled_grouped_amd import inputs
+    cfg = inputs.MoEConfig("ksteps", T=300, H=H, I=I, E=8, n_group=4, topk_group=2, topk=2, block_m=64)
+    print("layer K steps", H, I, flush=True)
+    x = inputs.make_moe_inputs(cfg, "cpu", seed=H + I)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    outs = {}
+    for BM in (16, 64, 128):
+        layer = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"], block_m=BM)
+        outs[BM] = layer.forward(g["hidden"], g["logits"]).clone()
+    torch.cuda.synchronize()
+    for BM in (64, 128):
+        assert torch.equal(outs[BM].view(torch.int16), outs[16].view(torch.int16)), BM
+    w, ids = oracle_routing(x, cfg)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(x["hidden"]))
+    ref, _, _, _ = oracle.moe.layer_tokens(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), x["w2"].numpy(),
+                                           x["w2_scale"].numpy(), ids, w)
+    assert_rel_max(f32_of_bf16(outs[64]), ref, what="layer H %d I %d" % (H, I))
+
+
 def test_dense_tiled_rejects(m):
     from fp8_block_scaled_grouped_amd import inputs
     d = inputs.make_dense_inputs(8, 256, 16512, DEV, seed=1)
