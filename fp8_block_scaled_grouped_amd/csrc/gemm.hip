@@ -69,6 +69,10 @@ struct Cfg {
   static constexpr int kSOff = kBOff + kBQ * 1024;
   static constexpr int kStage = kSOff + NW * kSD * 256;  // 64 fp32 A scales per scale DMA
   static constexpr int kLds = S * kStage;
+  // scale ring (the prefetching K loop with row-major activation scales): two slots, each
+  // 4 K blocks x 64 rows of fp32 scales (1 KB) per wave row, held in the scale regions of
+  // stages 0 and 1 (which the ring mode's stage DMAs leave alone)
+  static constexpr bool kRingFits = kWTM == 64 && WM * 1024 <= NW * kSD * 256 && S >= 2;
   // more than 4 row tiles per wave: A fragments are read one row tile at a time,
   // just ahead of the 4 MFMAs that use them, instead of all at the start of a step
   static constexpr bool kStreamA = kWTM / 16 > 4;
@@ -88,6 +92,15 @@ struct Cfg {
   static_assert(kLds + (MODE == kDown ? 2 : 1) * BM * 4 + kRed * kEpR * 4 <= 160 * 1024, "LDS of one workgroup");
 };
 
+
+// calls f(integral_constant<int, i>) for i = 0 .. N-1 in order
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
 
 // PK (dense only): K is not a multiple of 128, so the last K block holds
 // K % 128 bytes of each row.  The DMA pipeline walks the full blocks; the
@@ -126,9 +139,20 @@ __device__ uint32_t g_phase_trace[kTraceTiles][8][64][3];
 // One output tile (tile index `tile_id` of the launch grid) with the workgroup's LDS.
 // Every thread of the workgroup calls it with the same tile; it returns (uniformly)
 // for tiles past the problem.
-template <class C, int MODE, bool PK, bool BSH>
+//
+// SR (scale ring; the prefetching K loop on 64- and 128-row tiles, row-major activation
+// scales with a 16-byte aligned row stride, K blocks a multiple of 4): instead of every
+// wave fetching its rows' scales with a 4-byte DMA per K step (the waves of one wave row
+// all fetching the same 64 values), the first wave of each wave row fetches 4 K blocks
+// of its 64 rows' scales with one 16-byte DMA every fourth step into a two-slot LDS ring.
+// Same scale values, so the same results bit for bit; 8 DMA instructions per step fewer
+// on the 128-row tile.
+template <class C, int MODE, bool PK, bool BSH, bool SR = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_id, GemmSmem<C>& sm) {
   static_assert(!PK || MODE == kDense, "partial K blocks: dense mode only");
+  constexpr bool kPrefetch = !PK && !C::kStreamA && C::BM >= 64;
+  constexpr bool kSR = SR && kPrefetch && C::kRingFits;
+  static_assert(!SR || kSR, "the scale ring needs the prefetching K loop");
   static_assert(!(PK && BSH), "pre-shuffled B has whole 128x128 tiles");
   constexpr int64_t kBStep = BSH ? 128 * 128 : 128;  // bytes between K blocks of a B row
   // pre-shuffled B blocks are 1 KB copies from the first row of 8; their offset goes
@@ -286,6 +310,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
   }
   const uint8_t* s_base = uniform_ptr(g.a_scale);
   const int sofs = C::kSOff + w * C::kSD * 256;
+  // scale ring: K blocks [4 grp, 4 grp + 4) of wave row wm's scales into ring slot grp & 1,
+  // lane L moving row wm * 64 + L's 16 bytes.  Every wave of the row issues the same DMA (the
+  // same bytes to the same place), so that no branch on the wave splits the K step.
+  // ring slot s of wave row wm: the scale region of stage s
+  auto ring_ofs = [&](int slot) { return slot * C::kStage + C::kSOff + wm * 1024; };
+  const uint32_t soff_r = kSR ? (uint32_t)(a_row(wm * C::kWTM + lane) * g.ssm * 4) : 0u;
+  auto issue_scales = [&](int grp) {
+    dma16(s_base + (int64_t)(kbase + 4 * grp) * 4, soff_r, lds_addr(lds) + ring_ofs(grp & 1));
+  };
 
   vm_wait<0>();  // every ordinary load lands before the first DMA is queued
 
@@ -449,8 +482,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
   // which is refilled next), barrier (block kb + 1 is published and no wave reads block kb's
   // stage any more), refill block kb's stage with block kb + S, then block kb's MFMAs with
   // block kb + 1's reads between them.  All S stages are in flight ahead of the registers.
-  constexpr int L = C::kLoadsPerStage;
+  constexpr int L = kSR ? C::kQW : C::kLoadsPerStage;  // DMAs of a stage per wave
   static_assert(C::S * L < 64, "vmcnt range of the prefetching K loop");
+  auto issue_pf = [&](int stage, int kb) {
+#pragma unroll
+    for (int j = 0; j < L; ++j) issue_one(stage, kb, j);
+  };
   auto wait_blocks = [&](int a) {  // at most a blocks of this wave's DMAs still outstanding
     if (a >= 3) {
       vm_wait<3 * L>();
@@ -466,17 +503,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
     constexpr int TMV = decltype(tmv_c)::value;
     constexpr int NQ = TMV * C::kTN;
     static_assert(!C::kStreamA, "row tile fastest");
+    // (scale ring: the scales of blocks 0-3 go out ahead of block 0; a wait for block kb
+    // then also covers the scales of its group, which were issued before it)
+    if constexpr (kSR) issue_scales(0);
 #pragma unroll
     for (int s = 0; s < C::S; ++s)
-      if (s < KBp) issue(s, s);
+      if (s < KBp) issue_pf(s, s);
     v8i av[TMV > 0 ? TMV : 1], bv[C::kTN];
     v4f s4[TMV > 0 ? TMV : 1];
     auto sb_of = [&](int kb) {
       return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? sbv0 : sbv1), kb & 63));
     };
     auto read_a = [&](const uint8_t* st, int tm) { av[tm] = lds_frag(st + C::kAOff, wm * C::kWTM + tm * 16, lane); };
-    auto read_s = [&](const uint8_t* st, int tm, float sb) {
-      s4[tm] = *reinterpret_cast<const v4f*>(st + sofs + (tm * 16 + 4 * lg) * 4) * sb;
+    auto read_s = [&](const uint8_t* st, int tm, float sb, int kbr) {
+      if constexpr (kSR) {
+        // slot (kbr / 4) & 1, rows of 16 bytes (4 K blocks each)
+        const float* rg = reinterpret_cast<const float*>(lds + ring_ofs((kbr >> 2) & 1)) + (tm * 16 + 4 * lg) * 4 +
+                          (kbr & 3);
+        s4[tm] = v4f{rg[0], rg[4], rg[8], rg[12]} * sb;
+      } else {
+        s4[tm] = *reinterpret_cast<const v4f*>(st + sofs + (tm * 16 + 4 * lg) * 4) * sb;
+      }
     };
     auto read_b = [&](const uint8_t* st, int tn) { bv[tn] = lds_frag(st + C::kBOff, wn * C::kWTNB + tn * 16, lane); };
     wait_blocks(min(C::S - 1, KBp - 1));
@@ -486,7 +533,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
 #pragma unroll
       for (int tm = 0; tm < TMV; ++tm) {
         read_a(lds, tm);
-        read_s(lds, tm, sb);
+        read_s(lds, tm, sb, 0);
       }
 #pragma unroll
       for (int tn = 0; tn < C::kTN; ++tn) read_b(lds, tn);
@@ -519,7 +566,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
       const bool refill = RF == 1 || kb + C::S < KBp;
       const int nkb = kb + C::S;
       if constexpr (TMV == 0) {
-        if (refill) issue(stage, nkb);
+        if (refill) issue_pf(stage, nkb);
       } else {
         const uint8_t* nst = lds + ((stage + 1) % C::S) * C::kStage;
         const float sbn = NX ? sb_of(kb + 1) : 0.0f;
@@ -540,7 +587,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
           if constexpr (NX) {
             if (q < NQ && q % TMV == TMV - 1) read_b(nst, q / TMV);        // last use of bv[q / TMV]
             if (q < NQ && q / TMV == C::kTN - 1) read_a(nst, q % TMV);     // last use of av[q % TMV]
-            if (q >= 2 && (q - 2) / TMV == C::kTN - 1) read_s(nst, (q - 2) % TMV, sbn);  // its last fold
+            if (q >= 2 && (q - 2) / TMV == C::kTN - 1) read_s(nst, (q - 2) % TMV, sbn, kb + 1);  // its last fold
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -549,12 +596,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
     using One = std::integral_constant<int, 1>;
     using Zero = std::integral_constant<int, 0>;
     int kb0 = 0;
-    // rounds whose every step refills (kb + S < KBp for the round's last step)
+    // Scale ring: group ng (K blocks 4 ng .. 4 ng + 3) goes out at the start of a step s
+    // (before its wait) with 4 ng - 4 <= s <= 4 ng - 2.  From s >= 4 ng - 4: the slot's
+    // previous group (ng - 2) was last read during step 4 ng - 6, and those reads completed
+    // before the barrier of step 4 ng - 5.  From s <= 4 ng - 2: the group's first read is
+    // during step 4 ng - 1, whose wait leaves only the DMAs of step 4 ng - 2 outstanding.
+    // Rounds start every S = 3 steps, so each such window of 3 steps holds one, and the issue
+    // sits between steps, outside the MFMA sequences.
+    int ng = 1;
+    auto ring_issue = [&](int s) {
+      if constexpr (kSR) {
+        static_assert(!kSR || C::S <= 3, "one round start in every 3-step window");
+        if (4 * ng < KBp && s >= 4 * ng - 4) {
+          issue_scales(ng);
+          ++ng;
+        }
+      }
+    };
+    // rounds of S steps whose every step refills (kb + S < KBp for the round's last step)
     for (; kb0 + 2 * C::S - 1 < KBp; kb0 += C::S) {
-#pragma unroll
-      for (int u = 0; u < C::S; ++u) step(kb0 + u, u, One{}, One{});
+      ring_issue(kb0);
+      static_for<C::S>([&](auto uc) { step(kb0 + decltype(uc)::value, decltype(uc)::value, One{}, One{}); });
     }
     for (; kb0 < KBp; ++kb0) {
+      ring_issue(kb0);
       if (kb0 + 1 < KBp) {
         step(kb0, kb0 % C::S, Zero{}, One{});
       } else {
@@ -566,7 +631,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
   // the prefetching loop for whole K blocks on tiles of 64 rows or more; 16- and 32-row
   // tiles (decode-sized grouped blocks, split-K dense runs of a few K blocks) keep kloop,
   // whose shallower prologue measured no slower there, and so does the partial block of PK
-  constexpr bool kPrefetch = !PK && !C::kStreamA && C::BM >= 64;
   if constexpr (!kPrefetch) {
 #pragma unroll
     for (int s = 0; s < C::S - 1; ++s)
@@ -736,10 +800,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
   }
 }
 
-template <class C, int MODE, bool PK = false, bool BSH = false>
+template <class C, int MODE, bool PK = false, bool BSH = false, bool SR = false>
 __global__ __launch_bounds__(C::kThreads) void bs_gemm_kernel(GemmArgs g) {
   __shared__ GemmSmem<C> sm;
-  gemm_tile<C, MODE, PK, BSH>(g, blockIdx.x, sm);
+  gemm_tile<C, MODE, PK, BSH, SR>(g, blockIdx.x, sm);
 }
 
 // out[t, n] = bf16(sum_j y[t*k + j, n]), j ascending, fp32.  Writes nothing when
@@ -877,13 +941,28 @@ __global__ __launch_bounds__(CG::kThreads) void fused_moe_kernel(FusedArgs f) {
   }
 }
 
+// The scale ring (see gemm_tile) applies when the activation scales are row-major with a
+// row stride of whole 16-byte groups, 16-byte aligned, and every workgroup's K blocks
+// come in whole groups of 4.
+bool scale_ring_ok(const GemmArgs& g) {
+  const int64_t KB = ceil_div64(g.K, 128);
+  return g.sskb == 1 && g.ssm % 4 == 0 && (reinterpret_cast<uintptr_t>(g.a_scale) & 15u) == 0 && g.K % 128 == 0 &&
+         KB % 4 == 0 && g.kbs % 4 == 0;
+}
+
 template <class C, int MODE, bool PK, bool BSH>
 int launch_cfg(const GemmArgs& g, int64_t mblocks, hipStream_t stream) {
   if (MODE != kDense && g.N % C::kOutN != 0) return MOE355_EUNSUPPORTED;
   const int64_t grid = mblocks * ceil_div64(g.N, C::kOutN) * (MODE == kDense ? g.splits : 1);
   if (grid == 0) return MOE355_OK;
   MOE355_CHECK(grid < (1ll << 31), MOE355_EUNSUPPORTED);
-  hipLaunchKernelGGL((bs_gemm_kernel<C, MODE, PK, BSH>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, g);
+  constexpr bool kRingable = !PK && !C::kStreamA && C::BM >= 64 && C::kRingFits;
+  if (kRingable && scale_ring_ok(g)) {
+    hipLaunchKernelGGL((bs_gemm_kernel<C, MODE, PK, BSH, kRingable>), dim3((unsigned)grid), dim3(C::kThreads), 0,
+                       stream, g);
+  } else {
+    hipLaunchKernelGGL((bs_gemm_kernel<C, MODE, PK, BSH>), dim3((unsigned)grid), dim3(C::kThreads), 0, stream, g);
+  }
   return launch_status();
 }
 
