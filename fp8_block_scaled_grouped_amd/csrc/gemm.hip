@@ -279,10 +279,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
   static_assert(C::kAOff == 0 && C::kBOff == C::kAQ * 1024, "stage layout");
   static_assert(C::kAQ % C::NW == 0, "A/B split of the DMAs is the same in every wave");
   constexpr int kJA = C::kAQ / C::NW;
+  // kAOwn (the prefetching K loop): wave w moves A blocks 2w and 2w + 1, the rows of its own
+  // 16-row MFMA tile (tile wn of wave row wm), so a wave whose tile holds only padding skips
+  // its A DMAs altogether; otherwise wave w moves A blocks w, w + NW, ...
+  constexpr bool kAOwn = kPrefetch && kJA == 2 && C::kWTM == 16 * C::kWN && C::kAQ == C::kAQ0;
+  auto dma_block = [&](int j) { return kAOwn && j < kJA ? kJA * w + j : w + j * C::NW; };
+  // this wave's A rows hold at least one valid row (uniform)
+  const bool a_live = !kAOwn || 16 * w < nrows;
   uint32_t voff[C::kQW];
 #pragma unroll
   for (int j = 0; j < C::kQW; ++j) {
-    const int q = w + j * C::NW;
+    const int q = dma_block(j);
     const bool is_a = BSH ? j < kJA : q < C::kAQ;
     const int qq = is_a ? q : q - C::kAQ;
     const int r = qq * 8 + (lane >> 3);
@@ -330,7 +337,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
     const uint32_t base = lds0 + stage * C::kStage;
     const int64_t kg = kbase + kb;  // K block in the whole problem
     if (j < C::kQW) {
-      const int q = w + j * C::NW;
+      const int q = dma_block(j);
       if constexpr (kBUni) {
         if (j < kJA) {
           dma16(a_base + kg * 128, voff[j], base + q * 1024);
@@ -482,27 +489,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
   // which is refilled next), barrier (block kb + 1 is published and no wave reads block kb's
   // stage any more), refill block kb's stage with block kb + S, then block kb's MFMAs with
   // block kb + 1's reads between them.  All S stages are in flight ahead of the registers.
-  constexpr int L = kSR ? C::kQW : C::kLoadsPerStage;  // DMAs of a stage per wave
-  static_assert(C::S * L < 64, "vmcnt range of the prefetching K loop");
-  auto issue_pf = [&](int stage, int kb) {
-#pragma unroll
-    for (int j = 0; j < L; ++j) issue_one(stage, kb, j);
-  };
-  auto wait_blocks = [&](int a) {  // at most a blocks of this wave's DMAs still outstanding
-    if (a >= 3) {
-      vm_wait<3 * L>();
-    } else if (a == 2) {
-      vm_wait<2 * L>();
-    } else if (a == 1) {
-      vm_wait<L>();
-    } else {
-      vm_wait<0>();
-    }
-  };
-  auto kloop_pf = [&](auto tmv_c) {
+  // LA 0: this wave's A rows are all padding (kAOwn), so its DMAs of a stage are the B
+  // blocks (and scales) only, j = J0 .. J0 + L - 1
+  auto kloop_pf = [&](auto tmv_c, auto la_c) {
     constexpr int TMV = decltype(tmv_c)::value;
     constexpr int NQ = TMV * C::kTN;
     static_assert(!C::kStreamA, "row tile fastest");
+    constexpr int J0 = decltype(la_c)::value ? 0 : kJA;
+    static_assert(J0 == 0 || kAOwn, "A DMAs are skipped only where each wave moves its own tile's rows");
+    constexpr int L = (kSR ? C::kQW : C::kLoadsPerStage) - J0;  // DMAs of a stage per wave
+    static_assert(C::S * L < 64 && L > 0, "vmcnt range of the prefetching K loop");
+    auto issue_pf = [&](int stage, int kb) {
+#pragma unroll
+      for (int j = 0; j < L; ++j) issue_one(stage, kb, J0 + j);
+    };
+    auto wait_blocks = [&](int a) {  // at most a blocks of this wave's DMAs still outstanding
+      if (a >= 3) {
+        vm_wait<3 * L>();
+      } else if (a == 2) {
+        vm_wait<2 * L>();
+      } else if (a == 1) {
+        vm_wait<L>();
+      } else {
+        vm_wait<0>();
+      }
+    };
     // (scale ring: the scales of blocks 0-3 go out ahead of block 0; a wait for block kb
     // then also covers the scales of its group, which were issued before it)
     if constexpr (kSR) issue_scales(0);
@@ -579,7 +590,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
           if (q < NQ) tq[q % 3] = mfma16x16x128_fp8(av[q % TMV], bv[q / TMV], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int j = 0; j < L; ++j)
-            if (refill && (j * kGap < NQ + 1 ? j * kGap : NQ + 1) == q) issue_one(stage, nkb, j);
+            if (refill && (j * kGap < NQ + 1 ? j * kGap : NQ + 1) == q) issue_one(stage, nkb, J0 + j);
           if (q >= 2) {
             const int pq = q - 2;
             acc[pq % TMV][pq / TMV] += tq[pq % 3] * s4[pq % TMV];
@@ -608,7 +619,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
       if constexpr (kSR) {
         static_assert(!kSR || C::S <= 3, "one round start in every 3-step window");
         if (4 * ng < KBp && s >= 4 * ng - 4) {
-          issue_scales(ng);
+          // the first wave of the row fetches the group; the others see it behind the barrier
+          // of step 4 ng - 1, which follows its wait for its DMAs of the steps before
+          if (wn == 0) issue_scales(ng);
           ++ng;
         }
       }
@@ -637,8 +650,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
       if (s < KBp) issue(s, s);
   }
   auto kloop_any = [&](auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
+    using One = std::integral_constant<int, 1>;
+    using Zero = std::integral_constant<int, 0>;
     if constexpr (kPrefetch) {
-      kloop_pf(tmv_c);
+      if constexpr (!kAOwn || TMV == C::kTM) {
+        kloop_pf(tmv_c, One{});  // (every tile of a full wave row holds valid rows)
+      } else if constexpr (TMV == 0) {
+        kloop_pf(tmv_c, Zero{});
+      } else {
+        if (a_live) {
+          kloop_pf(tmv_c, One{});
+        } else {
+          kloop_pf(tmv_c, Zero{});
+        }
+      }
     } else {
       kloop(tmv_c);
     }
