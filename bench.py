@@ -17,7 +17,10 @@ weights is reported beside it (object "decode", roofline on HBM).
 
 --sweep block_m times the whole layer for every M tile over a range of token
 counts (the table behind moe_block_m); --sweep dense times the dense GEMM on
-the linear-layer shapes of a DeepSeek-V3 layer.  Sweeps print one JSON line
+the linear-layer shapes of a DeepSeek-V3 layer; --sweep tiles times the two
+grouped GEMMs on hand-built sorted buffers whose 128-row blocks hold r valid
+rows each (the cost of a tile against its live rows, with weights shared by
+2 or 16 blocks of an expert or read by one block only).  Sweeps print one JSON line
 per measurement and no bench line.
 """
 import argparse
@@ -45,7 +48,7 @@ def parse():
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--tokens", type=int, default=None, help="token count of a MoE workload (default: its own)")
     ap.add_argument("--no-decode", action="store_true", help="prefill: leave out the decode layer beside it")
-    ap.add_argument("--sweep", choices=["block_m", "dense"], default=None)
+    ap.add_argument("--sweep", choices=["block_m", "dense", "tiles"], default=None)
     ap.add_argument("--phases", action="store_true",
                     help="per-step phase clocks of the gate/up kernel from the diagnostic library libmoe355_trace.so")
     ap.add_argument("--graph", action="store_true",
@@ -401,6 +404,57 @@ def sweep_block_m(a):
             del tm
 
 
+def sweep_tiles(a):
+    """Grouped GEMM time per 128-row tile against its valid rows r: sorted buffers built on the
+    host (blocks of 128 rows, the first r of each valid, distinct random pairs of the 8192-token
+    prefill layer, the rest the sentinel), with the block's expert chosen so that 2 blocks
+    ("pairs") or 16 blocks ("shared16") of one expert share its weights, or every block has an
+    expert of its own ("solo")."""
+    import torch
+
+    import fp8_block_scaled_grouped_amd as m
+    cfg = moe_config("prefill")
+    dev = torch.device("cuda:0")
+    x = moe_inputs(cfg, a.seed)
+    T, k, E, H, I, BM = cfg.T, cfg.topk, cfg.E, cfg.H, cfg.I, 128
+    a8, a_s = m.fp8_quant_1x128(x["hidden"])
+    ms = m.moe_sort_sizes(T, k, E, BM)[0]
+    h8 = torch.zeros((ms, I), dtype=torch.uint8, device=dev)
+    hs = torch.ones((ms, I // 128), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(m.moe_down_combine_workspace(T, H, k), dtype=torch.uint8, device=dev)
+    gen = torch.Generator().manual_seed(a.seed + 1)
+    perm = torch.randperm(T * k, generator=gen).to(torch.int32)
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        return t[n // 2]
+
+    cases = [("pairs", 512, r, lambda b: b // 2) for r in (128, 96, 64, 32, 16, 1)]
+    cases += [(lay, 256, r, f) for r in (128, 32, 1) for lay, f in (("solo", lambda b: b), ("shared16", lambda b: b // 16))]
+    for lay, nblk, r, expert_of in cases:
+        sid = torch.full((ms,), T * k, dtype=torch.int32)
+        for b in range(nblk):
+            sid[b * BM:b * BM + r] = perm[b * r:(b + 1) * r]
+        seid = torch.tensor([expert_of(b) for b in range(nblk)] + [0] * (ms // BM - nblk), dtype=torch.int32)
+        sid, seid = sid.to(dev), seid.to(dev)
+        sw = torch.full((ms,), 0.5, dtype=torch.float32, device=dev)
+        nv = torch.tensor([nblk * BM], dtype=torch.int32, device=dev)
+        g = timed(lambda: m.moe_fp8_blockscale_g1u1(a8, a_s, x["w1"], x["w1_scale"], sid, seid, nv, k, BM, h8, hs))
+        d = timed(lambda: m.moe_down_combine(h8, hs, x["w2"], x["w2_scale"], sid, sw, seid, nv, T, k, BM, out, ws))
+        print(json.dumps({"sweep": "tiles", "layout": lay, "blocks": nblk, "rows_per_block": r, "g1u1_ms": g,
+                          "down_combine_ms": d, "g1u1_us_per_tile_per_cu": g * 1e3 * 256 / (nblk * (2 * I // 256)),
+                          "down_tiles": nblk * (H // 256)}), flush=True)
+
+
 # (N, K) of the linear layers of a DeepSeek-V3 layer
 V3_LINEAR = [("q_a_proj", 1536, 7168), ("kv_a_proj", 576, 7168), ("q_b_proj", 24576, 1536),
              ("kv_b_proj", 32768, 512), ("o_proj", 7168, 16384), ("dense_mlp_gate_up", 36864, 7168),
@@ -645,6 +699,9 @@ def main():
         return
     if a.sweep == "dense":
         sweep_dense(a)
+        return
+    if a.sweep == "tiles":
+        sweep_tiles(a)
         return
     if a.phases:
         phases(a)
