@@ -669,3 +669,63 @@ def test_dense_small_m_kernel(m, M, N, K, layout):
     assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
     ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
     assert_rel_max(f32_of_bf16(c1), ref, what="dense small-M %dx%dx%d" % (M, N, K))
+
+
+# Row-major activation scales (with K blocks in whole groups of 4) go through the scale ring
+# of the 64- and 128-row tiles; K-block-major scales, K splits off groups of 4 and the 16-row
+# tiles keep a scale DMA per stage.  Both carry the same values, so every variant gives the
+# same bits.  K of 8 to 28 blocks puts the ring's groups at every phase of the 3-step rounds.
+@pytest.mark.parametrize("K", [1024, 2048, 2560, 3072, 3584])
+def test_scale_ring_dense_bit_identical(m, K):
+    from fp8_block_scaled_grouped_amd import inputs
+    M, N = 300, 512
+    print("scale ring dense", M, N, K, flush=True)
+    d = inputs.make_dense_inputs(M, N, K, "cpu", seed=K + 5)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(d["a"]))
+    ref = oracle.gemm.gemm_blockscale(a8, sa, d["b"].numpy(), d["b_scale"].numpy())
+    b8, bs = d["b"].to(DEV), d["b_scale"].to(DEV)
+    a8d = torch.from_numpy(a8).to(DEV)
+    outs = {}
+    for layout in ("row", "kblock"):
+        sad = torch.from_numpy(sa).to(DEV) if layout == "row" else torch.from_numpy(np.ascontiguousarray(sa.T)).to(DEV)
+        for bm in (16, 64, 128):
+            c = m.gemm_fp8_blockscale_tiled(a8d, sad, b8, bs, bm, 256, 1, scale_layout=layout)
+            torch.cuda.synchronize()
+            outs[(layout, bm)] = c.view(torch.int16).cpu()
+    first = outs[("kblock", 16)]
+    for key, v in outs.items():
+        assert torch.equal(v, first), key
+    assert_rel_max(f32_of_bf16(first.view(torch.bfloat16)), ref, what="scale ring dense K %d" % K)
+
+
+# The grouped GEMMs with H and I multiples of 512 take the scale ring for row-major scales
+# (gate/up: the activations' scales; down: h's scales, always row-major); with K-block-major
+# activation scales gate/up keeps the per-stage scale DMA.  h and the output must agree bit for
+# bit between the two, and with the oracle.
+@pytest.mark.parametrize("BM", [64, 128])
+def test_scale_ring_grouped_bit_identical(m, BM):
+    from fp8_block_scaled_grouped_amd import inputs
+    cfg = inputs.MoEConfig("ring", T=300, H=1536, I=1024, E=16, n_group=4, topk_group=2, topk=4, block_m=BM)
+    print("scale ring grouped", BM, flush=True)
+    x = inputs.make_moe_inputs(cfg, "cpu", seed=BM)
+    g = {k: v.to(DEV) for k, v in x.items()}
+    res = {}
+    for layout in ("row", "kblock"):
+        layer = m.MoELayer(cfg, g["bias"], g["w1"], g["w1_scale"], g["w2"], g["w2_scale"], block_m=BM,
+                           scale_layout=layout)
+        out = layer.forward(g["hidden"], g["logits"])
+        torch.cuda.synchronize()
+        # h rows of routed pairs (padding rows of a block are never written)
+        nv = int(layer.sort_out[3].item())
+        live = np.zeros(layer.max_sorted, bool)
+        live[:nv] = layer.sort_out[0].cpu().numpy()[:nv] < cfg.T * cfg.topk
+        res[layout] = (out.view(torch.int16).cpu(), np_u8(layer.h8)[live], layer.h_scale.cpu().numpy()[live])
+    assert res["row"][1].shape[0] == cfg.T * cfg.topk
+    assert torch.equal(res["row"][0], res["kblock"][0])
+    assert np.array_equal(res["row"][1], res["kblock"][1])
+    assert np.array_equal(res["row"][2], res["kblock"][2])
+    w, ids = oracle_routing(x, cfg)
+    a8, sa = oracle.quant.quant_1x128(f32_of_bf16(x["hidden"]))
+    ref, _, _, _ = oracle.moe.layer_tokens(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), x["w2"].numpy(),
+                                           x["w2_scale"].numpy(), ids, w)
+    assert_rel_max(f32_of_bf16(res["row"][0].view(torch.bfloat16)), ref, what="scale ring layer")
