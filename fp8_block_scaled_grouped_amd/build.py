@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe355.so")
 TRACE_LIB = os.path.join(PKG, "libmoe355_trace.so")
 # standalone probe programs (tuning/<name>.hip -> <package>/<name>)
-PROBES = ["lds_fill_probe", "kstep_probe"]
+PROBES = ["lds_fill_probe", "kstep_probe", "e4m3_cvt_check"]
 SOURCES = ["gemm.hip", "gemm_big.hip", "dense_small.hip", "topk.hip", "sort.hip", "quant.hip", "shuffle.hip", "status.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -32,6 +32,18 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return sign | r;
 }
 
+// Four fp32 values -> their e4m3 codes (byte i = value i) by the hardware conversion
+// (v_cvt_pk_fp8_f32: OCP e4m3, nearest-even).  On every finite fp32 with |y| <= 460 it gives
+// exactly f32_to_e4m3's code (an exhaustive check over all such bit patterns,
+// tuning/e4m3_cvt_check.hip), so inputs are first clamped to +-460, which leaves their codes
+// unchanged (everything from 448 up saturates to 448).  Inputs are finite.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+  auto cl = [](float y) { return __builtin_amdgcn_fmed3f(y, -460.0f, 460.0f); };
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), r, true);
+  return (uint32_t)r;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // fp32 -> bf16 bits, nearest-even (finite inputs; NaN kept quiet).

@@ -814,8 +814,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
         uint32_t wds[kCPI / 4];
 #pragma unroll
         for (int v = 0; v < kCPI / 4; ++v)
-          wds[v] = f32_to_e4m3(h[4 * v] / sc) | (f32_to_e4m3(h[4 * v + 1] / sc) << 8) |
-                   (f32_to_e4m3(h[4 * v + 2] / sc) << 16) | (f32_to_e4m3(h[4 * v + 3] / sc) << 24);
+          wds[v] = f32x4_to_e4m3(h[4 * v] / sc, h[4 * v + 1] / sc, h[4 * v + 2] / sc, h[4 * v + 3] / sc);
         uint8_t* dst = g.h8 + (row0 + rt) * g.N + nt * 128 + qc * kCPI;
 #pragma unroll
         for (int v = 0; v < kCPI / 16; ++v)

@@ -333,8 +333,7 @@ __global__ __launch_bounds__(kThr) void big_gemm_kernel(GemmArgs g) {
         for (int wt = 0; wt < kWT; ++wt) {
           const v4f h = acc[wt][t];
           *reinterpret_cast<uint32_t*>(hq + r * kHRS + 16 * wt + 4 * lg) =
-              f32_to_e4m3(h[0] / sc[t]) | (f32_to_e4m3(h[1] / sc[t]) << 8) | (f32_to_e4m3(h[2] / sc[t]) << 16) |
-              (f32_to_e4m3(h[3] / sc[t]) << 24);
+              f32x4_to_e4m3(h[0] / sc[t], h[1] / sc[t], h[2] / sc[t], h[3] / sc[t]);
         }
       }
     }

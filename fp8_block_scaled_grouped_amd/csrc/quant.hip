@@ -40,11 +40,8 @@ __global__ __launch_bounds__(kThreads) void quant_1x128_kernel(const uint16_t* _
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
   const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(f[i] / s) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(f[4 + i] / s) << (8 * i);
+  const uint32_t lo = f32x4_to_e4m3(f[0] / s, f[1] / s, f[2] / s, f[3] / s);
+  const uint32_t hi = f32x4_to_e4m3(f[4] / s, f[5] / s, f[6] / s, f[7] / s);
   if (live) *reinterpret_cast<uint2*>(q + m * ld_q + kb * 128 + sub * 8) = make_uint2(lo, hi);
   if (sub == 0) scale[m * ssm + kb * sskb] = s;
 }

@@ -210,7 +210,7 @@ def test_trace_library_exports():
     assert fn(None, 1) == -1  # host-side check, no GPU touched
 
 
-@pytest.mark.parametrize("name", ["lds_fill_probe", "kstep_probe"])
+@pytest.mark.parametrize("name", ["lds_fill_probe", "kstep_probe", "e4m3_cvt_check"])
 def test_probes_built_for_gfx950(name):
     # the probe programs are built with the library; their device code must be gfx950 code
     # objects (checked from the bundle's target names)
