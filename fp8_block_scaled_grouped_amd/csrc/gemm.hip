@@ -318,9 +318,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int64_t tile_
   const uint8_t* s_base = uniform_ptr(g.a_scale);
   const int sofs = C::kSOff + w * C::kSD * 256;
   // scale ring: K blocks [4 grp, 4 grp + 4) of wave row wm's scales into ring slot grp & 1,
-  // lane L moving row wm * 64 + L's 16 bytes.  Every wave of the row issues the same DMA (the
-  // same bytes to the same place), so that no branch on the wave splits the K step.
-  // ring slot s of wave row wm: the scale region of stage s
+  // lane L moving row wm * 64 + L's 16 bytes.  Group 0 goes out from every wave of the row
+  // with the pipeline prologue (the same bytes to the same place); later groups from the row's
+  // first wave only, between K steps.  Ring slot s of wave row wm: the scale region of stage s.
   auto ring_ofs = [&](int slot) { return slot * C::kStage + C::kSOff + wm * 1024; };
   const uint32_t soff_r = kSR ? (uint32_t)(a_row(wm * C::kWTM + lane) * g.ssm * 4) : 0u;
   auto issue_scales = [&](int grp) {
