@@ -12,10 +12,10 @@ struct BlockMTuned {
 };
 
 static const BlockMTuned kBlockMTuned[] = {
-    {2, 16},  // 16:1.019 32:1.029 64:1.053 128:1.084 256:1.376
-    {4, 32},  // 16:1.280 32:1.266 64:1.290 128:1.325 256:1.678
-    {16, 64},  // 16:1.905 32:1.687 64:1.655 128:1.671 256:2.063
-    {256, 128},  // 16:13.926 32:8.908 64:6.529 128:5.395 256:5.890
+    {2, 16},  // 16:1.009 32:1.021 64:1.036 128:1.053 256:1.308
+    {4, 32},  // 16:1.265 32:1.255 64:1.274 128:1.295 256:1.607
+    {16, 64},  // 16:1.862 32:1.651 64:1.620 128:1.625 256:2.072
+    {256, 128},  // 16:13.516 32:8.564 64:5.912 128:4.756 256:5.504
 };
 
 }  // namespace moe355
