@@ -729,3 +729,19 @@ def test_scale_ring_grouped_bit_identical(m, BM):
     ref, _, _, _ = oracle.moe.layer_tokens(a8, sa, x["w1"].numpy(), x["w1_scale"].numpy(), x["w2"].numpy(),
                                            x["w2_scale"].numpy(), ids, w)
     assert_rel_max(f32_of_bf16(res["row"][0].view(torch.bfloat16)), ref, what="scale ring layer")
+
+
+# The e4m3 encoder the kernels use (the hardware conversion after a clamp) equals the
+# integer-op nearest-even encoder on every finite fp32 bit pattern, at every byte position of
+# its packed result: the check program built with the library runs the comparison on the GPU.
+def test_e4m3_encoder_exhaustive():
+    import json
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "fp8_block_scaled_grouped_amd",
+                       "e4m3_cvt_check")
+    assert os.path.exists(exe), "build the library first (python -m fp8_block_scaled_grouped_amd.build)"
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    line = [x for x in r.stdout.splitlines() if x.startswith("{")][-1]
+    res = json.loads(line)
+    assert r.returncode == 0 and res["mismatches"] == 0, res
